@@ -1,0 +1,314 @@
+"""CPU oracle for Star Attention's two-phase attention hot path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call anything in ``oracle/``.  The HIP library never calls it and
+shares no code with it: the only thing both sides use is the seeded input
+generator in ``workloads/``, which holds none of the method's arithmetic.
+
+Everything here is plain float64 numpy: explicit boolean masks, one matmul
+per score matrix, no tiling, no fusion, no reordering beyond what the
+definitions state.  Every function is pinned by ``tests/test_oracle_pins.py``
+against closed forms, brute force, library routines (torch SDPA in float64)
+or facts the pages fix; no function here is "parity unpinned".
+
+Sources (cited by page title and section):
+  [SA-pith]   Pith review of "Star Attention: Efficient LLM Inference over
+              Long Sequences" (pith.science) -- "What carries the argument",
+              "Core claim", "Referee Report", "Circularity Check",
+              "Assumptions & free parameters", the abstract.
+  [SA-atlas]  atlas.scime.ai summary of the same paper -- "Approach",
+              "Measured effects reported in the paper".
+  [SA-repo]   graphcanon record of the NVIDIA/Star-Attention repository --
+              README excerpt (Phase 1 / Phase 2 description; HuggingFace
+              Transformers implementation).
+  [Pulsar]    Pith review of "Dropping the Anchor ... Pulsar Attention" --
+              "Core claim", "Assumptions & free parameters" (restates Star's
+              KV-cache identity and the exactness of the online-softmax merge).
+
+Readings where the pages leave a step open (all listed in the design notes):
+  * causality inside an augmented block: causal over the concatenation
+    [anchor ; block], so every block row sees the whole anchor;
+  * the anchor is the first ``a`` context tokens at their original positions
+    (a = b by default), hence its keys/values are block 1's rotated K/V;
+  * a tail block shorter than b when b does not divide L; b >= L is one block;
+  * softmax scale 1/sqrt(D); GQA query head h reads KV head h // g;
+  * the softmax statistic is the natural-log log-sum-exp of the scaled scores;
+  * the query host is the last partition: it also holds the query and decode
+    tokens' KV, and a token attends to itself;
+  * RoPE is rotate-half with theta_j = base^(-2j/D), angles in exact (fp64)
+    arithmetic, no frequency scaling.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------
+# RoPE at original position ids
+# ----------------------------------------------------------------------------
+def rope_theta(D: int, base: float) -> np.ndarray:
+    """Rotation frequencies theta_j = base^(-2j/D), j = 0..D/2-1 (float64)."""
+    j = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * j / D)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate-half RoPE of ``x[..., S, D]`` at integer positions ``pos[S]``.
+
+    Pair (j, j + D/2) is rotated by the angle pos * theta_j.  Positions are
+    the tokens' original (global) ids: [SA-pith] "What carries the argument"
+    (the anchor keeps the first block's positional indices) and [Pulsar]
+    "Assumptions & free parameters" (original position ids preserve RoPE
+    geometry).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * rope_theta(D, base)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# masked softmax attention: the one primitive every step uses
+# ----------------------------------------------------------------------------
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
+           scale: float):
+    """Softmax attention of rows ``q[n, D]`` over ``k, v[m, D]`` where
+    ``mask[n, m]`` marks the visible keys.
+
+    Returns ``(o[n, D], lse[n])`` with ``lse`` the natural-log log-sum-exp of
+    the scaled visible scores.  A row with no visible key gets o = 0 and
+    lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, m = q.shape[0], k.shape[0]
+    assert mask.shape == (n, m)
+    o = np.zeros((n, v.shape[1]), dtype=np.float64)
+    lse = np.full(n, NEG_INF, dtype=np.float64)
+    if n == 0 or m == 0:
+        return o, lse
+    s = (q @ k.T) * scale
+    s = np.where(mask, s, NEG_INF)
+    mx = s.max(axis=1)
+    live = np.isfinite(mx)
+    if not live.any():
+        return o, lse
+    s, mx = s[live], mx[live]
+    p = np.exp(s - mx[:, None])
+    l = p.sum(axis=1)
+    o[live] = (p @ v) / l[:, None]
+    lse[live] = mx + np.log(l)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Phase 1: blockwise-local attention with the anchor block
+# ----------------------------------------------------------------------------
+def blocks(L: int, b: int):
+    """Context blocks c_1..c_n as [start, end) token ranges; the last one is
+    shorter when b does not divide L ([SA-pith] "What carries the argument":
+    the context is split into blocks of b tokens)."""
+    return [(s, min(s + b, L)) for s in range(0, L, b)]
+
+
+def phase1_block_keys(i: int, L: int, b: int, a: int):
+    """Key ids and explicit mask of the augmented block c'_i (0-based i).
+
+    c'_1 = c_1 is plain causal attention over b tokens ([SA-pith] "Referee
+    Report", minor comment on section 2.1: only blocks after the first carry
+    the anchor).  For i >= 1 the augmented block is [anchor ; c_i]: every row
+    sees all ``a`` anchor tokens (the first ``a`` context tokens at their
+    original positions) plus its own block's tokens up to itself.
+    Returns (key_ids[m], mask[n_i, m]).
+    """
+    s, e = blocks(L, b)[i]
+    n = e - s
+    own = np.arange(s, e)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    if i == 0:
+        return own, causal
+    anc = np.arange(0, min(a, L))
+    mask = np.concatenate([np.ones((n, anc.size), dtype=bool), causal], axis=1)
+    return np.concatenate([anc, own]), mask
+
+
+def phase1(Q, K, V, b: int, a: int, scale: float):
+    """Phase 1 context encoding ([SA-pith] "What carries the argument",
+    "Referee Report" summary; [SA-repo] README, Phase 1).
+
+    Q [B, Hq, L, D], K/V [B, Hkv, L, D] (already rotated).  Each block's rows
+    attend within their augmented block only.  Returns O [B, Hq, L, D] and
+    LSE [B, Hq, L].  The anchor's own outputs are not produced: block 1's
+    rows are the only outputs for those tokens.
+    """
+    B, Hq, L, D = Q.shape
+    g = Hq // K.shape[1]
+    O = np.zeros((B, Hq, L, D))
+    LSE = np.full((B, Hq, L), NEG_INF)
+    for i, (s, e) in enumerate(blocks(L, b)):
+        keys, mask = phase1_block_keys(i, L, b, a)
+        for bb in range(B):
+            for h in range(Hq):
+                o, l = attend(Q[bb, h, s:e], K[bb, h // g, keys],
+                              V[bb, h // g, keys], mask, scale)
+                O[bb, h, s:e], LSE[bb, h, s:e] = o, l
+    return O, LSE
+
+
+def phase1_rows(q_rows, pos, K, V, b: int, a: int, scale: float):
+    """Phase 1 outputs for selected rows of one (batch, query head).
+
+    ``q_rows[n, D]`` are rotated query rows at context positions ``pos[n]``;
+    ``K, V [L, D]`` are that head's KV head.  Each row is computed over the
+    same key set and the same mask row as in :func:`phase1`.
+    """
+    L = K.shape[0]
+    pos = np.asarray(pos)
+    o = np.zeros((pos.size, V.shape[1]))
+    lse = np.full(pos.size, NEG_INF)
+    for i, (s, e) in enumerate(blocks(L, b)):
+        sel = np.nonzero((pos >= s) & (pos < e))[0]
+        if sel.size == 0:
+            continue
+        keys, mask = phase1_block_keys(i, L, b, a)
+        oo, ll = attend(q_rows[sel], K[keys], V[keys], mask[pos[sel] - s], scale)
+        o[sel], lse[sel] = oo, ll
+    return o, lse
+
+
+def kv_cache_entries(L: int, b: int) -> int:
+    """Number of KV entries kept after Phase 1: each host keeps only its own
+    block and the anchor's KV is discarded ([SA-atlas] "Approach"; [Pulsar]
+    "Core claim": exactly L entries across hosts)."""
+    return sum(e - s for s, e in blocks(L, b))
+
+
+# ----------------------------------------------------------------------------
+# Phase 2: per-partition partials and the exact LSE merge
+# ----------------------------------------------------------------------------
+def partitions(L: int, b: int, cache_len: int):
+    """KV partitions ("hosts"): partition j holds block j's KV; the last one
+    (the query host) also holds the query and generated tokens' KV
+    ([SA-pith] "What carries the argument": a designated query host)."""
+    parts = blocks(L, b)
+    s, _ = parts[-1]
+    parts[-1] = (s, cache_len)
+    return parts
+
+
+def partial(q, q_pos, Kc, Vc, k0: int, k1: int, scale: float):
+    """Local attention of query rows over cache entries [k0, k1): the
+    per-host output A_h and statistic s_h ([SA-pith] "Circularity Check":
+    each host computes a local attention output and softmax denominator).
+
+    ``q[n, D]`` rotated rows at positions ``q_pos[n]``; ``Kc, Vc [N, D]``.
+    A key at cache index c (= its position) is visible to a row at position
+    p when c <= p.
+    """
+    keys = np.arange(k0, k1)
+    mask = keys[None, :] <= np.asarray(q_pos)[:, None]
+    return attend(q, Kc[k0:k1], Vc[k0:k1], mask, scale)
+
+
+def lse_merge(o_parts, lse_parts):
+    """Exact online-softmax merge of N partials ([SA-pith] "Referee Report",
+    minor comment on Algorithm 2: the weight of A_h is exp(s_h - s_global);
+    "Circularity Check": the reweighting is an exact identity).
+
+    ``o_parts[N, ..., D]``, ``lse_parts[N, ...]``.  s = log sum_h exp(s_h);
+    A = sum_h exp(s_h - s) A_h.  Partials with s_h = -inf carry no weight; if
+    every partial is -inf the row is o = 0, lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    live = np.isfinite(m)
+    msafe = np.where(live, m, 0.0)
+    w = np.exp(lse_parts - msafe[None])          # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    lse = np.where(live, msafe + np.log(np.where(live, tot, 1.0)), NEG_INF)
+    wn = np.where(live[None], w / np.where(live, tot, 1.0)[None], 0.0)
+    o = (wn[..., None] * o_parts).sum(axis=0)
+    return o, lse
+
+
+def phase2(q, q_pos, Kc, Vc, parts, scale: float):
+    """Sequence-global attention of query rows via per-partition partials
+    and the LSE merge ([SA-pith] "Referee Report" summary, Eqs. 3-4;
+    [SA-repo] README, Phase 2).  Returns (o, lse, o_parts, lse_parts)."""
+    op, lp = [], []
+    for (k0, k1) in parts:
+        o, l = partial(q, q_pos, Kc, Vc, k0, k1, scale)
+        op.append(o)
+        lp.append(l)
+    op, lp = np.stack(op), np.stack(lp)
+    o, l = lse_merge(op, lp)
+    return o, l, op, lp
+
+
+# ----------------------------------------------------------------------------
+# textbook references used only as pins
+# ----------------------------------------------------------------------------
+def dense_causal(Q, K, V, scale: float):
+    """Plain dense causal attention of one head, [S, D] each (global
+    attention, the method's baseline)."""
+    S = Q.shape[0]
+    return attend(Q, K, V, np.tril(np.ones((S, S), dtype=bool)), scale)
+
+
+# ----------------------------------------------------------------------------
+# the whole hot path on one workload (small workloads only)
+# ----------------------------------------------------------------------------
+def star_attention(w, x: dict, splits_ranges=None):
+    """Run both phases on a workload's inputs (see ``workloads.inputs``).
+
+    ``x`` maps names to float64 arrays.  Returns a dict with the rotated
+    tensors, Phase-1 O/LSE, the query-phase partials and merged output, and
+    one merged output per decode step.
+    """
+    B, Hq, Hkv, D, L = w.B, w.Hq, w.Hkv, w.D, w.L
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    rot = (lambda t, pos: rope(t, pos, w.base)) if w.rope else (lambda t, pos: np.asarray(t, np.float64))
+    pos_ctx = np.arange(L)
+    pos_q = L + np.arange(w.Lq)
+    pos_d = L + w.Lq + np.arange(w.T)
+    Q, K = rot(x["q"], pos_ctx), rot(x["k"], pos_ctx)
+    V = np.asarray(x["v"], np.float64)
+    O1, LSE1 = phase1(Q, K, V, w.b, w.a, scale)
+    qq, kq = rot(x["qq"], pos_q), rot(x["kq"], pos_q)
+    qd, kd = rot(x["qd"], pos_d), rot(x["kd"], pos_d)
+    Kc = np.concatenate([K, kq, kd], axis=2)
+    Vc = np.concatenate([V, np.asarray(x["vq"], np.float64),
+                         np.asarray(x["vd"], np.float64)], axis=2)
+    res = {"Q": Q, "K": K, "V": V, "O1": O1, "LSE1": LSE1, "Kc": Kc, "Vc": Vc,
+           "qq": qq, "qd": qd}
+    parts_q = partitions(L, w.b, L + w.Lq)
+    O2 = np.zeros((B, Hq, w.Lq, D))
+    L2 = np.zeros((B, Hq, w.Lq))
+    P2o = np.zeros((len(parts_q), B, Hq, w.Lq, D))
+    P2l = np.zeros((len(parts_q), B, Hq, w.Lq))
+    OD = np.zeros((B, Hq, w.T, D))
+    LD = np.zeros((B, Hq, w.T))
+    for bb in range(B):
+        for h in range(Hq):
+            kv = h // g
+            o, l, op, lp = phase2(qq[bb, h], pos_q, Kc[bb, kv], Vc[bb, kv],
+                                  parts_q, scale)
+            O2[bb, h], L2[bb, h], P2o[:, bb, h], P2l[:, bb, h] = o, l, op, lp
+            for t in range(w.T):
+                parts_t = partitions(L, w.b, L + w.Lq + t + 1)
+                o, l, _, _ = phase2(qd[bb, h, t:t + 1], pos_d[t:t + 1],
+                                    Kc[bb, kv], Vc[bb, kv], parts_t, scale)
+                OD[bb, h, t], LD[bb, h, t] = o[0], l[0]
+    res.update(O2=O2, LSE2=L2, P2o=P2o, P2l=P2l, OD=OD, LSED=LD)
+    return res
