@@ -1,0 +1,165 @@
+"""MI355X (gfx950) Star Attention hot path.
+
+Thin PyTorch-facing binding of the C ABI in ``include/star_attn.h``: the
+functions below only turn torch tensors into ``star_tensor`` descriptors,
+pick the current HIP stream and call the library.  Every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device
+memory and streams only; tensors must live on a ROCm device.
+
+Phase 1 -- anchor-block blockwise-local causal attention (context encoding).
+Phase 2 -- per-partition partials + exact LSE merge (query and decode).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
+
+__all__ = ["rope_apply", "kv_append", "phase1_blocklocal", "phase2_partial",
+           "lse_merge", "split_ranges", "StarError", "library"]
+
+
+def library():
+    return _lib.load()
+
+
+def _desc(t: torch.Tensor) -> _lib.StarTensor:
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, H, S, D] tensor, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    if t.dtype == torch.bfloat16:
+        dt = _lib.STAR_BF16
+    elif t.dtype == torch.float32:
+        dt = _lib.STAR_F32
+    else:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the head dim must be contiguous")
+    B, H, S, D = t.shape
+    return _lib.StarTensor(t.data_ptr(), dt, 0, B, H, S, D,
+                           t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def rope_apply(x: torch.Tensor, pos: torch.Tensor | None = None, pos0: int = 0,
+               base: float = 500000.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rotate-half RoPE of ``x[B, H, S, D]`` at positions ``pos[S]`` (int64,
+    device) or ``pos0 + s``.  In place when ``out`` is None."""
+    out = x if out is None else out
+    if pos is not None:
+        if pos.dtype != torch.int64 or pos.numel() != x.shape[2] or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous int64 tensor of length S")
+    a, b = _desc(x), _desc(out)
+    st = library().star_rope_apply(ctypes.byref(a), ctypes.byref(b), _ptr(pos), int(pos0),
+                                   float(base), _stream(x))
+    _lib.check("star_rope_apply", st)
+    return out
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, slot0: int, pos0: int,
+              base: float = 500000.0, rope: bool = True):
+    """Rotate ``k_new`` at positions ``pos0 + t`` and write it, with
+    ``v_new``, into cache rows ``slot0 + t``."""
+    d = [_desc(t) for t in (k_new, v_new, k_cache, v_cache)]
+    st = library().star_kv_append(*[ctypes.byref(x) for x in d], int(slot0), int(pos0),
+                                  float(base), int(bool(rope)), _stream(k_new))
+    _lib.check("star_kv_append", st)
+
+
+def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,
+                      scale: float | None = None, out=None, lse=None,
+                      want_lse: bool = False):
+    """Phase 1 context encoding.  Returns ``(o, lse)`` (lse None unless
+    ``want_lse`` or an ``lse`` buffer is given)."""
+    B, Hq, L, D = q.shape
+    if anchor_len is None:
+        anchor_len = block_b
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq * L):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, L] tensor")
+    dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
+    st = library().star_phase1_blocklocal(
+        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(block_b), int(anchor_len),
+        float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
+    _lib.check("star_phase1_blocklocal", st)
+    return out, lse
+
+
+def split_ranges(part_offsets, splits: int):
+    """The [start, end) key range of every chunk, in o_part order: partition
+    j is cut into chunks of roundup(ceil(n_j / splits), 64) keys."""
+    out = []
+    for j in range(len(part_offsets) - 1):
+        a, b = int(part_offsets[j]), int(part_offsets[j + 1])
+        c = -(-(b - a) // splits)
+        c = -(-c // STAR_SPLIT_ALIGN) * STAR_SPLIT_ALIGN
+        for s in range(splits):
+            lo = a + s * c
+            out.append((min(lo, b), min(lo + c, b)))
+    return out
+
+
+def phase2_partial(q, k_cache, v_cache, part_offsets, splits: int = 1, q_pos0: int = 0,
+                   scale: float | None = None, o_part=None, lse_part=None):
+    """Per-chunk partials of query rows ``q[B, Hq, Lq, D]`` (at positions
+    ``q_pos0 + r``) over the cache partitions ``part_offsets[P + 1]``.
+    Returns ``(o_part[P*splits, B, Hq, Lq, D], lse_part[P*splits, B, Hq, Lq])``."""
+    B, Hq, Lq, D = q.shape
+    P = len(part_offsets) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    N = P * splits
+    if o_part is None:
+        o_part = torch.empty((N, B, Hq, Lq, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((N, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    for t, n in ((o_part, N * B * Hq * Lq * D), (lse_part, N * B * Hq * Lq)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+            raise ValueError("o_part / lse_part must be contiguous fp32 buffers of the full size")
+    offs = (ctypes.c_int64 * (P + 1))(*[int(x) for x in part_offsets])
+    dq, dk, dv = _desc(q), _desc(k_cache), _desc(v_cache)
+    st = library().star_phase2_partial(
+        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), offs, int(P), int(splits),
+        int(q_pos0), float(scale), _ptr(o_part), _ptr(lse_part), _stream(q))
+    _lib.check("star_phase2_partial", st)
+    return o_part, lse_part
+
+
+def lse_merge(o_part, lse_part, out=None, lse=None, out_dtype=torch.float32,
+              want_lse: bool = True):
+    """Exact LSE merge over the leading (partial) dim of ``o_part[N, B, H, S, D]``.
+    Returns ``(o[B, H, S, D], lse[B, H, S])``."""
+    N, B, H, S, D = o_part.shape
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part and lse_part must be contiguous")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise TypeError("partials are fp32")
+    if tuple(lse_part.shape) != (N, B, H, S):
+        raise ValueError("lse_part shape mismatch")
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=out_dtype, device=o_part.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_part.device)
+    do = _desc(out)
+    st = library().star_lse_merge(_ptr(o_part), _ptr(lse_part), int(N), ctypes.byref(do),
+                                  _ptr(lse), _stream(o_part))
+    _lib.check("star_lse_merge", st)
+    return out, lse

@@ -1,0 +1,292 @@
+// C ABI of the Star Attention hot path: argument validation on the host,
+// then dispatch to the gfx950 kernels on the caller's stream.  The entry
+// points are declared and documented in include/star_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/star_attn.h"
+#include "internal.h"
+
+namespace {
+
+using star::TensorRef;
+
+int esize(int32_t dtype) { return dtype == STAR_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Basic checks of one tensor descriptor.
+int check_tensor(const star_tensor* t, bool allow_f32) {
+  if (t == nullptr || t->data == nullptr) return STAR_ERR_NULL;
+  if (t->dtype != STAR_BF16 && !(allow_f32 && t->dtype == STAR_F32)) return STAR_ERR_DTYPE;
+  if (t->B < 1 || t->H < 1 || t->S < 0 || t->D < 1) return STAR_ERR_SHAPE;
+  if (t->sB < 0 || t->sH < 0 || t->sS < 0) return STAR_ERR_SHAPE;
+  const int64_t e = esize(t->dtype);
+  if (!aligned16(t->data)) return STAR_ERR_ALIGN;
+  if ((t->sB * e) % 16 || (t->sH * e) % 16 || (t->sS * e) % 16) return STAR_ERR_ALIGN;
+  return STAR_OK;
+}
+
+TensorRef ref(const star_tensor* t) { return TensorRef{t->data, t->sB, t->sH, t->sS}; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
+
+bool rope_dim_ok(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
+
+void fill_inv_freq(double* inv_freq, int64_t D, double base) {
+  for (int64_t j = 0; j < D / 2; ++j) inv_freq[j] = std::pow(base, -2.0 * (double)j / (double)D);
+  for (int64_t j = D / 2; j < 64; ++j) inv_freq[j] = 0.0;
+}
+
+// Shared validation of q/k/v for the attention entry points.
+int check_qkv(const star_tensor* q, const star_tensor* k, const star_tensor* v) {
+  int s;
+  if ((s = check_tensor(q, true)) != STAR_OK) return s;
+  if ((s = check_tensor(k, true)) != STAR_OK) return s;
+  if ((s = check_tensor(v, true)) != STAR_OK) return s;
+  if (k->dtype != q->dtype || v->dtype != q->dtype) return STAR_ERR_DTYPE;
+  if (q->D != 64 && q->D != 128) return STAR_ERR_UNSUPPORTED;
+  if (k->D != q->D || v->D != q->D) return STAR_ERR_SHAPE;
+  if (k->B != q->B || v->B != q->B) return STAR_ERR_SHAPE;
+  if (k->H != v->H || k->S != v->S) return STAR_ERR_SHAPE;
+  if (q->H % k->H != 0) return STAR_ERR_SHAPE;
+  if (q->H / k->H > 16) return STAR_ERR_UNSUPPORTED;
+  if (q->B > 65535 || q->H > 65535) return STAR_ERR_UNSUPPORTED;
+  return STAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* star_status_string(int status) {
+  switch (status) {
+    case STAR_OK: return "STAR_OK";
+    case STAR_ERR_NULL: return "STAR_ERR_NULL: a required pointer is NULL";
+    case STAR_ERR_SHAPE: return "STAR_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case STAR_ERR_DTYPE: return "STAR_ERR_DTYPE: unsupported dtype or dtype combination";
+    case STAR_ERR_ALIGN: return "STAR_ERR_ALIGN: data or stride not 16-byte aligned";
+    case STAR_ERR_UNSUPPORTED: return "STAR_ERR_UNSUPPORTED: valid request this build does not serve";
+    case STAR_ERR_HIP: return "STAR_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown star_status";
+  }
+}
+
+int star_abi_version(void) { return 100; }
+
+int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
+                    int64_t pos0, double base, void* stream) {
+  int s;
+  if ((s = check_tensor(x_in, true)) != STAR_OK) return s;
+  if ((s = check_tensor(x_out, true)) != STAR_OK) return s;
+  if (x_out->dtype != x_in->dtype) return STAR_ERR_DTYPE;
+  if (x_out->B != x_in->B || x_out->H != x_in->H || x_out->S != x_in->S || x_out->D != x_in->D)
+    return STAR_ERR_SHAPE;
+  if (!rope_dim_ok(x_in->D)) return STAR_ERR_UNSUPPORTED;
+  if (!(base > 1.0) || !std::isfinite(base)) return STAR_ERR_SHAPE;
+  if (pos == nullptr && pos0 < 0) return STAR_ERR_SHAPE;
+  if (x_in->B > 65535 || x_in->H > 65535) return STAR_ERR_UNSUPPORTED;
+  if (x_in->S == 0) return STAR_OK;
+  star::RopeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = ref(x_in);
+  p.y = x_out->data;
+  p.ysB = x_out->sB;
+  p.ysH = x_out->sH;
+  p.ysS = x_out->sS;
+  p.B = (int32_t)x_in->B;
+  p.H = (int32_t)x_in->H;
+  p.D = (int32_t)x_in->D;
+  p.S = x_in->S;
+  p.f32 = x_in->dtype == STAR_F32;
+  p.pos = pos;
+  p.pos0 = pos0;
+  fill_inv_freq(p.inv_freq, x_in->D, base);
+  return hip_status(star::launch_rope(p, (hipStream_t)stream));
+}
+
+int star_kv_append(const star_tensor* k_new, const star_tensor* v_new, const star_tensor* k_cache,
+                   const star_tensor* v_cache, int64_t slot0, int64_t pos0, double base,
+                   int32_t rope, void* stream) {
+  int s;
+  if ((s = check_tensor(k_new, false)) != STAR_OK) return s;
+  if ((s = check_tensor(v_new, false)) != STAR_OK) return s;
+  if ((s = check_tensor(k_cache, false)) != STAR_OK) return s;
+  if ((s = check_tensor(v_cache, false)) != STAR_OK) return s;
+  const int64_t B = k_new->B, H = k_new->H, T = k_new->S, D = k_new->D;
+  if (v_new->B != B || v_new->H != H || v_new->S != T || v_new->D != D) return STAR_ERR_SHAPE;
+  if (k_cache->B != B || k_cache->H != H || k_cache->D != D) return STAR_ERR_SHAPE;
+  if (v_cache->B != B || v_cache->H != H || v_cache->D != D || v_cache->S != k_cache->S)
+    return STAR_ERR_SHAPE;
+  if (!rope_dim_ok(D)) return STAR_ERR_UNSUPPORTED;
+  if (slot0 < 0 || pos0 < 0 || slot0 + T > k_cache->S) return STAR_ERR_SHAPE;
+  if (rope && (!(base > 1.0) || !std::isfinite(base))) return STAR_ERR_SHAPE;
+  if (B > 65535 || H > 65535) return STAR_ERR_UNSUPPORTED;
+  if (T == 0) return STAR_OK;
+  star::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.kn = ref(k_new);
+  p.vn = ref(v_new);
+  p.kc = k_cache->data;
+  p.vc = v_cache->data;
+  p.kcsB = k_cache->sB; p.kcsH = k_cache->sH; p.kcsS = k_cache->sS;
+  p.vcsB = v_cache->sB; p.vcsH = v_cache->sH; p.vcsS = v_cache->sS;
+  p.B = (int32_t)B;
+  p.H = (int32_t)H;
+  p.D = (int32_t)D;
+  p.T = T;
+  p.slot0 = slot0;
+  p.pos0 = pos0;
+  p.rope = rope != 0;
+  if (rope) fill_inv_freq(p.inv_freq, D, base);
+  return hip_status(star::launch_append(p, (hipStream_t)stream));
+}
+
+int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const star_tensor* v,
+                           int64_t block_b, int64_t anchor_len, float scale,
+                           const star_tensor* o, float* lse, void* stream) {
+  int s;
+  if ((s = check_qkv(q, k, v)) != STAR_OK) return s;
+  if ((s = check_tensor(o, false)) != STAR_OK) return s;
+  if (k->S != q->S) return STAR_ERR_SHAPE;
+  if (o->B != q->B || o->H != q->H || o->S != q->S || o->D != q->D) return STAR_ERR_SHAPE;
+  if (block_b < 1 || anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  if (q->S == 0) return STAR_OK;
+  star::FlashParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = ref(q);
+  p.k = ref(k);
+  p.v = ref(v);
+  p.B = (int32_t)q->B;
+  p.Hq = (int32_t)q->H;
+  p.Hkv = (int32_t)k->H;
+  p.g = p.Hq / p.Hkv;
+  p.D = (int32_t)q->D;
+  p.in_f32 = q->dtype == STAR_F32;
+  p.q_rows = q->S;
+  p.kv_rows = k->S;
+  p.pos_shift = 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mode = 0;
+  p.L = q->S;
+  p.b = block_b < q->S ? block_b : q->S;
+  p.a = anchor_len < p.b ? anchor_len : p.b;
+  if (block_b >= q->S) p.a = 0;  // a single block has no anchor
+  p.o = o->data;
+  p.osB = o->sB;
+  p.osH = o->sH;
+  p.osS = o->sS;
+  p.lse = lse;
+  return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
+                        const star_tensor* v_cache, const int64_t* part_offsets, int32_t P,
+                        int32_t splits, int64_t q_pos0, float scale, float* o_part,
+                        float* lse_part, void* stream) {
+  int s;
+  if ((s = check_qkv(q, k_cache, v_cache)) != STAR_OK) return s;
+  if (part_offsets == nullptr || o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
+  if (P < 1 || P > STAR_MAX_PARTS || splits < 1 || splits > 1024) return STAR_ERR_SHAPE;
+  if (q_pos0 < 0) return STAR_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
+  if (part_offsets[0] < 0 || part_offsets[P] > k_cache->S) return STAR_ERR_SHAPE;
+  for (int j = 0; j < P; ++j)
+    if (part_offsets[j + 1] < part_offsets[j]) return STAR_ERR_SHAPE;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return STAR_ERR_ALIGN;
+  if (q->S == 0) return STAR_OK;
+  int64_t chunk[STAR_MAX_PARTS];
+  for (int j = 0; j < P; ++j) {
+    const int64_t n = part_offsets[j + 1] - part_offsets[j];
+    int64_t c = (n + splits - 1) / splits;
+    c = (c + STAR_SPLIT_ALIGN - 1) / STAR_SPLIT_ALIGN * STAR_SPLIT_ALIGN;
+    chunk[j] = c;
+  }
+  const int g = (int)(q->H / k_cache->H);
+  if (star::decode_supported(g, q->S, (int)q->D)) {
+    star::DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = ref(q);
+    p.k = ref(k_cache);
+    p.v = ref(v_cache);
+    p.B = (int32_t)q->B;
+    p.Hq = (int32_t)q->H;
+    p.Hkv = (int32_t)k_cache->H;
+    p.g = g;
+    p.D = (int32_t)q->D;
+    p.in_f32 = q->dtype == STAR_F32;
+    p.Lq = q->S;
+    p.kv_rows = k_cache->S;
+    p.q_pos0 = q_pos0;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.P = P;
+    p.splits = splits;
+    for (int j = 0; j <= P; ++j) p.offs[j] = part_offsets[j];
+    for (int j = 0; j < P; ++j) p.chunk[j] = chunk[j];
+    p.opart = o_part;
+    p.lse = lse_part;
+    return hip_status(star::launch_decode(p, (hipStream_t)stream));
+  }
+  star::FlashParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = ref(q);
+  p.k = ref(k_cache);
+  p.v = ref(v_cache);
+  p.B = (int32_t)q->B;
+  p.Hq = (int32_t)q->H;
+  p.Hkv = (int32_t)k_cache->H;
+  p.g = g;
+  p.D = (int32_t)q->D;
+  p.in_f32 = q->dtype == STAR_F32;
+  p.q_rows = q->S;
+  p.kv_rows = k_cache->S;
+  p.pos_shift = q_pos0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mode = 1;
+  p.P = P;
+  p.splits = splits;
+  for (int j = 0; j <= P; ++j) p.offs[j] = part_offsets[j];
+  for (int j = 0; j < P; ++j) p.chunk[j] = chunk[j];
+  p.lse = lse_part;
+  p.opart = o_part;
+  return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_lse_merge(const float* o_part, const float* lse_part, int32_t N, const star_tensor* o,
+                   float* lse, void* stream) {
+  if (o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
+  int s;
+  if ((s = check_tensor(o, true)) != STAR_OK) return s;
+  if (N < 1 || N > 65536) return STAR_ERR_SHAPE;
+  if (o->D != 64 && o->D != 128) return STAR_ERR_UNSUPPORTED;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return STAR_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  const int64_t R = o->B * o->H * o->S;
+  if (R == 0) return STAR_OK;
+  star::MergeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.opart = o_part;
+  p.lsep = lse_part;
+  p.N = N;
+  p.R = R;
+  p.D = (int32_t)o->D;
+  p.H = (int32_t)o->H;
+  p.S = o->S;
+  p.o = o->data;
+  p.o_f32 = o->dtype == STAR_F32;
+  p.osB = o->sB;
+  p.osH = o->sH;
+  p.osS = o->sS;
+  p.lse = lse;
+  return hip_status(star::launch_merge(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

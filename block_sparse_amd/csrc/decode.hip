@@ -1,0 +1,255 @@
+// Split-KV Phase-2 partials for few query rows per KV head (decode steps).
+//
+// A generated token attends globally to every cached token; each KV
+// partition returns its local output and log-sum-exp (Pith review of Star
+// Attention, "Core claim" and "Circularity Check").  With one query token
+// the work is a stream over the whole KV cache, so this kernel is built to
+// keep HBM busy: every workgroup owns one chunk of one partition for one KV
+// head and all of its g query heads (GQA heads share each K/V byte read),
+// its four waves walk interleaved 32-key tiles of the chunk, and each wave
+// prefetches its next tile into registers (16-byte loads, 4 lanes per
+// 64-byte run of a key row) while it computes the current one.
+//
+// Math on v_mfma_f32_16x16x32_bf16 with the g*Lq query rows padded to 16:
+// S^T = K Q^T (A = K straight from the loaded registers), the row
+// max/sum per lane column, then O^T += V^T P^T where V^T is read from a
+// per-wave LDS copy of the V tile (keys permuted to match the order the
+// S^T registers hold them) and P^T comes from the S^T registers.  The four
+// waves merge their (m, l, O) in LDS at the end.
+#include "common.h"
+#include "internal.h"
+
+namespace star {
+namespace {
+
+constexpr int NWD = 4;      // waves per workgroup
+constexpr int KTD = 32;     // keys per wave tile
+constexpr float kRescaleLog2 = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ int v_off(int key, int d) {
+  return key * (D * 2) + ((((d >> 3) ^ (key & 15)) & (D / 8 - 1)) << 4) + ((d & 7) << 1);
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) {
+  constexpr int NDC = D / 32;   // k-steps of 32 along D
+  constexpr int NDB = D / 16;   // 16-row blocks of O^T
+  // per-wave V tiles during the key loop; reused for the final merge
+  static_assert(NWD * 16 * D * 4 <= NWD * KTD * D * 2, "merge buffer must fit");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NWD * KTD * D * 2];
+  __shared__ float red_m[NWD][16];
+  __shared__ float red_l[NWD][16];
+  float (*red_o)[16][D] = reinterpret_cast<float (*)[16][D]>(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;       // query row (column of S^T / O^T)
+  const int kg = lane >> 4;      // 8-wide k group of the MFMA operands
+
+  const int lid = xcd_remap(blockIdx.x, p.total_items);
+  const int nch = p.P * p.splits;
+  const int cs = lid % nch;
+  const int rr = lid / nch;
+  const int kvh = rr % p.Hkv;
+  const int b = rr / p.Hkv;
+  const int part = cs / p.splits, sp = cs - part * p.splits;
+  const int64_t c0 = p.offs[part] + (int64_t)sp * p.chunk[part];
+  int64_t c1 = min(c0 + p.chunk[part], p.offs[part + 1]);
+  c1 = min(c1, p.kv_rows);
+  if (c1 < c0) c1 = c0;
+
+  const int nrows = p.g * (int)p.Lq;
+  const bool row_ok = n < nrows;
+  const int hh = n % p.g;
+  const int qi = n / p.g;
+  const int head = kvh * p.g + hh;
+  const int64_t qpos = p.q_pos0 + qi;
+  // smallest row position (rows are ordered by query index)
+  const int64_t min_qpos = p.q_pos0;
+
+  // Q^T as the B operand: lane (row n, group kg) holds d = 32dc + 8kg + e.
+  bf16x8 qf[NDC];
+  {
+    const T* qr = reinterpret_cast<const T*>(p.q.data) + (int64_t)b * p.q.sB +
+                  (int64_t)(row_ok ? head : 0) * p.q.sH + (int64_t)(row_ok ? qi : 0) * p.q.sS;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      u32x4 v = {0, 0, 0, 0};
+      if (row_ok) v = Load8<T>::load(qr + 32 * dc + 8 * kg);
+      qf[dc] = as_bf16x8(v);
+    }
+  }
+
+  const T* kbase = reinterpret_cast<const T*>(p.k.data) + (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH;
+  const T* vbase = reinterpret_cast<const T*>(p.v.data) + (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH;
+
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY, lsum = 0.f;
+  const float c2 = p.scale_log2;
+
+  const int nt = (int)((c1 - c0 + KTD - 1) / KTD);
+  uint8_t* vs = smem + wave * (KTD * D * 2);
+
+  // register staging for one tile: [key block (16 keys)][d chunk]
+  u32x4 kr[2][NDC], vr[2][NDC];
+  auto load_tile = [&](int t) {
+    const int64_t kt = c0 + (int64_t)KTD * t;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t key = kt + 16 * kb + n;
+      const bool ok = key < c1;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        kr[kb][dc] = u32x4{0, 0, 0, 0};
+        vr[kb][dc] = u32x4{0, 0, 0, 0};
+        if (ok) {
+          kr[kb][dc] = Load8<T>::load(kbase + key * p.k.sS + 32 * dc + 8 * kg);
+          vr[kb][dc] = Load8<T>::load(vbase + key * p.v.sS + 32 * dc + 8 * kg);
+        }
+      }
+    }
+  };
+
+  int t = wave;
+  if (t < nt) load_tile(t);
+  for (; t < nt; t += NWD) {
+    const int64_t kt = c0 + (int64_t)KTD * t;
+    // S^T = K Q^T for two 16-key blocks
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma16(as_bf16x8(kr[kb][dc]), qf[dc], s[kb]);
+    }
+    // stage V (row-major, chunk-swizzled) in this wave's LDS region
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const int key = 16 * kb + n;
+        const int d = 32 * dc + 8 * kg;
+        *reinterpret_cast<u32x4*>(vs + v_off<D>(key, d)) = vr[kb][dc];
+      }
+    asm volatile("" ::: "memory");
+    // prefetch this wave's next tile while the current one is computed
+    if (t + NWD < nt) load_tile(t + NWD);
+
+    // mask: keys past the chunk end or after the row's position
+    if (kt + KTD > c1 || kt + KTD - 1 > min_qpos) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t key = kt + 16 * kb + 4 * kg + j;
+          if (key >= c1 || key > qpos) s[kb][j] = -INFINITY;
+        }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mt2 = mt * c2;
+    const bool need = mt2 > m2 + kRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
+      if (need) m2 = mt2;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float msub = (m2 == -INFINITY) ? 0.f : m2;
+    bf16x8 pt;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], c2, -msub));
+        lsum += pv;
+        pt[4 * kb + j] = (__bf16)pv;
+      }
+    // O^T += V^T P^T : lane (d = 16db + n, group kg) supplies keys
+    // 4kg + e (e < 4) and 16 + 4kg + (e - 4), matching pt's order.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 16 * db + n;
+      bf16x8 a;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = (e < 4) ? (4 * kg + e) : (16 + 4 * kg + e - 4);
+        a[e] = *reinterpret_cast<const __bf16*>(vs + v_off<D>(key, d));
+      }
+      oacc[db] = mfma16(a, pt, oacc[db]);
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- merge the four waves' (m, l, O^T) and write the chunk partial
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // every wave is done with its V tile
+  if (kg == 0) {
+    red_m[wave][n] = m2;
+    red_l[wave][n] = lsum;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red_o[wave][n][16 * db + 4 * kg + j] = oacc[db][j];
+  __syncthreads();
+
+  // thread -> (row, d) pairs
+  for (int idx = tid; idx < 16 * D; idx += NWD * 64) {
+    const int r = idx / D, d = idx - r * D;
+    if (r >= nrows) continue;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWD; ++w) mm = fmaxf(mm, red_m[w][r]);
+    float l = 0.f, o = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NWD; ++w) {
+        const float al = (red_m[w][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_m[w][r] - mm);
+        l += al * red_l[w][r];
+        o += al * red_o[w][r][d];
+      }
+    }
+    const int rh = r % p.g, rq = r / p.g;
+    const int64_t row = (((int64_t)cs * p.B + b) * p.Hq + (kvh * p.g + rh)) * p.Lq + rq;
+    p.opart[row * D + d] = l > 0.f ? o / l : 0.f;
+    if (d == 0) p.lse[row] = l > 0.f ? (mm + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool decode_supported(int g, int64_t Lq, int D) {
+  return (D == 64 || D == 128) && g >= 1 && Lq >= 1 && (int64_t)g * Lq <= 16;
+}
+
+hipError_t launch_decode(DecodeParams& p, hipStream_t stream) {
+  const int64_t items = (int64_t)p.B * p.Hkv * p.P * p.splits;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  p.total_items = (int32_t)items;
+  const dim3 grid(p.total_items), block(NWD * 64);
+  if (p.D == 128) {
+    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<128, float>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<128, __bf16>), grid, block, 0, stream, p);
+  } else {
+    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<64, float>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<64, __bf16>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace star

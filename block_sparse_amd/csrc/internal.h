@@ -1,0 +1,113 @@
+// Host-side launch interfaces between the C ABI (abi.cpp) and the kernels.
+// Every struct here is passed to its kernel by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/star_attn.h"
+
+namespace star {
+
+struct TensorRef {
+  const void* data;
+  int64_t sB, sH, sS;
+};
+
+// Flash-style attention over analytic key ranges (Phase 1 and the Phase-2
+// query chunk).
+struct FlashParams {
+  TensorRef q, k, v;
+  int32_t B, Hq, Hkv, g;
+  int32_t D;
+  int32_t in_f32;        // Q/K/V are fp32 (rounded to bf16 on load)
+  int64_t q_rows;        // rows of the q tensor
+  int64_t kv_rows;       // rows of the k/v tensors
+  int64_t pos_shift;     // position of q row r is r + pos_shift
+  float scale;           // softmax scale on raw scores
+  float scale_log2;      // scale * log2(e)
+  // workgroup geometry (filled by the launcher)
+  int32_t gw, npg, hgroups, m_pos;
+  int32_t total_items;
+  // mode 0: Phase 1 ; mode 1: Phase-2 partials
+  int32_t mode;
+  // Phase 1
+  int64_t L, b, a;
+  int32_t nblocks, nqt_full, nqt_last, nqt0;
+  // Phase 2
+  int32_t P, splits, nqt2;
+  int64_t offs[STAR_MAX_PARTS + 1];
+  int64_t chunk[STAR_MAX_PARTS];  // split chunk length per partition
+  // outputs
+  void* o;               // Phase 1 O (bf16)
+  int64_t osB, osH, osS;
+  float* lse;            // Phase 1 lse (nullable) or Phase-2 lse_part
+  float* opart;          // Phase-2 o_part
+};
+
+hipError_t launch_flash(FlashParams& p, hipStream_t stream);
+
+// Split-KV decode partials (few query rows per KV head).
+struct DecodeParams {
+  TensorRef q, k, v;
+  int32_t B, Hq, Hkv, g, D;
+  int32_t in_f32;
+  int64_t Lq;
+  int64_t kv_rows;
+  int64_t q_pos0;
+  float scale, scale_log2;
+  int32_t P, splits;
+  int64_t offs[STAR_MAX_PARTS + 1];
+  int64_t chunk[STAR_MAX_PARTS];
+  int32_t total_items;
+  float* opart;
+  float* lse;
+};
+
+bool decode_supported(int g, int64_t Lq, int D);
+hipError_t launch_decode(DecodeParams& p, hipStream_t stream);
+
+struct RopeParams {
+  TensorRef x;
+  void* y;
+  int64_t ysB, ysH, ysS;
+  int32_t B, H, D;
+  int64_t S;
+  int32_t f32;
+  const int64_t* pos;
+  int64_t pos0;
+  double inv_freq[64];
+};
+
+hipError_t launch_rope(RopeParams& p, hipStream_t stream);
+
+struct AppendParams {
+  TensorRef kn, vn;
+  void* kc;
+  void* vc;
+  int64_t kcsB, kcsH, kcsS, vcsB, vcsH, vcsS;
+  int32_t B, H, D;
+  int64_t T, slot0, pos0;
+  int32_t rope;
+  double inv_freq[64];
+};
+
+hipError_t launch_append(AppendParams& p, hipStream_t stream);
+
+struct MergeParams {
+  const float* opart;
+  const float* lsep;
+  int32_t N;
+  int64_t R;             // rows = B * H * S
+  int32_t D;
+  int32_t H;
+  int64_t S;
+  void* o;
+  int32_t o_f32;
+  int64_t osB, osH, osS;
+  float* lse;
+};
+
+hipError_t launch_merge(MergeParams& p, hipStream_t stream);
+
+}  // namespace star

@@ -1,0 +1,179 @@
+// RoPE at original position ids, and the KV-cache append of new tokens.
+//
+// Every token is rotated at its true position: the anchor block keeps the
+// first block's positions and query/generated tokens continue after the
+// context (Pith review of Star Attention, "What carries the argument";
+// Pith review of Pulsar Attention, "Assumptions & free parameters": original
+// position ids preserve RoPE geometry).  Rotate-half form: pair (j, j+D/2)
+// turns by pos * theta_j.
+//
+// The angle pos * theta_j reaches ~1e6 rad at million-token positions, where
+// an fp32 product is off by up to ~5e-2 rad.  Here it is formed and reduced
+// modulo 2*pi in fp64 (two-constant Cody-Waite step), so the fp32 angle
+// handed to sincosf is within ~1e-7 rad of the exact one.
+//
+// Both kernels are HBM-bound streams: a thread owns 8 pairs of one row
+// (two 16-byte loads for bf16), computes their sin/cos once and applies them
+// to every head of that position, so the trigonometry is amortised over H.
+#include "common.h"
+#include "internal.h"
+
+namespace star {
+namespace {
+
+constexpr double kTwoPiHi = 6.283185307179586;          // fp64(2*pi)
+constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189535;
+
+__device__ __forceinline__ void rope_angle(double pos, double inv_freq, float& c, float& s) {
+  const double ang = pos * inv_freq;
+  const double k = rint(ang * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, ang);
+  r = fma(-k, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* out) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf16_lo(w[i]);
+    out[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* out) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = a[i];
+    out[4 + i] = b[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* in);
+template <>
+__device__ __forceinline__ void store8<__bf16>(__bf16* p, const float* in) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16(in[2 * i], in[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* in) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{in[0], in[1], in[2], in[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{in[4], in[5], in[6], in[7]};
+}
+
+// grid-stride over (b, s, pair-chunk); loop over heads inside
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(const RopeParams p) {
+  const int nchunk = p.D / 16;  // chunks of 8 pairs per row
+  const int64_t total = (int64_t)p.B * p.S * nchunk;
+  const int half = p.D / 2;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int ch = (int)(idx % nchunk);
+    const int64_t bs = idx / nchunk;
+    const int64_t s = bs % p.S;
+    const int b = (int)(bs / p.S);
+    const double pos = (double)(p.pos ? p.pos[s] : p.pos0 + s);
+    float cs[8], sn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rope_angle(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
+    const T* xb = reinterpret_cast<const T*>(p.x.data) + (int64_t)b * p.x.sB + s * p.x.sS;
+    T* yb = reinterpret_cast<T*>(p.y) + (int64_t)b * p.ysB + s * p.ysS;
+    for (int h = 0; h < p.H; ++h) {
+      const T* xr = xb + (int64_t)h * p.x.sH;
+      T* yr = yb + (int64_t)h * p.ysH;
+      float x1[8], x2[8], y1[8], y2[8];
+      load8<T>(xr + 8 * ch, x1);
+      load8<T>(xr + half + 8 * ch, x2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y1[i] = x1[i] * cs[i] - x2[i] * sn[i];
+        y2[i] = x2[i] * cs[i] + x1[i] * sn[i];
+      }
+      store8<T>(yr + 8 * ch, y1);
+      store8<T>(yr + half + 8 * ch, y2);
+    }
+  }
+}
+
+// one thread per (b, h, t, pair-chunk): rotate k_t, copy v_t, into the cache
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  const int nchunk = p.D / 16;
+  const int64_t total = (int64_t)p.B * p.H * p.T * nchunk;
+  const int half = p.D / 2;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int ch = (int)(idx % nchunk);
+    int64_t r = idx / nchunk;
+    const int64_t t = r % p.T;
+    r /= p.T;
+    const int h = (int)(r % p.H);
+    const int b = (int)(r / p.H);
+    const __bf16* kr = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
+                       (int64_t)h * p.kn.sH + t * p.kn.sS;
+    const __bf16* vr = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
+                       (int64_t)h * p.vn.sH + t * p.vn.sS;
+    __bf16* kc = reinterpret_cast<__bf16*>(p.kc) + (int64_t)b * p.kcsB + (int64_t)h * p.kcsH +
+                 (p.slot0 + t) * p.kcsS;
+    __bf16* vc = reinterpret_cast<__bf16*>(p.vc) + (int64_t)b * p.vcsB + (int64_t)h * p.vcsH +
+                 (p.slot0 + t) * p.vcsS;
+    *reinterpret_cast<u32x4*>(vc + 8 * ch) = *reinterpret_cast<const u32x4*>(vr + 8 * ch);
+    *reinterpret_cast<u32x4*>(vc + half + 8 * ch) = *reinterpret_cast<const u32x4*>(vr + half + 8 * ch);
+    float x1[8], x2[8], y1[8], y2[8];
+    load8<__bf16>(kr + 8 * ch, x1);
+    load8<__bf16>(kr + half + 8 * ch, x2);
+    if (p.rope) {
+      const double pos = (double)(p.pos0 + t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float c, s;
+        rope_angle(pos, p.inv_freq[8 * ch + i], c, s);
+        y1[i] = x1[i] * c - x2[i] * s;
+        y2[i] = x2[i] * c + x1[i] * s;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y1[i] = x1[i];
+        y2[i] = x2[i];
+      }
+    }
+    store8<__bf16>(kc + 8 * ch, y1);
+    store8<__bf16>(kc + half + 8 * ch, y2);
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_rope(RopeParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.B * p.S * (p.D / 16);
+  if (total <= 0 || p.H <= 0) return hipSuccess;
+  if (p.f32)
+    hipLaunchKernelGGL(rope_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(rope_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(AppendParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.B * p.H * p.T * (p.D / 16);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(grid_for(total)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace star

@@ -1,0 +1,189 @@
+/*
+ * star_attn.h -- C ABI of the MI355X (gfx950) Star Attention hot path.
+ *
+ * Star Attention runs long-context inference in two phases:
+ *   Phase 1 (context encoding): the context is cut into blocks of b tokens;
+ *     every block after the first is prefixed with an anchor block (the
+ *     first block, at its original position ids) and attends causally within
+ *     that augmented block only; the anchor's KV is then discarded.
+ *   Phase 2 (query and generation): query and generated tokens attend to
+ *     every cached token; each KV partition ("host") produces a local output
+ *     and a log-sum-exp, and an exact online-softmax merge combines them.
+ * Sources: Pith review of "Star Attention: Efficient LLM Inference over Long
+ * Sequences" ("What carries the argument", "Referee Report", "Circularity
+ * Check", "Assumptions & free parameters"); the atlas.scime.ai summary of
+ * the same paper ("Approach"); the NVIDIA/Star-Attention repository README
+ * (graphcanon record).  On one GPU the hosts are KV partitions resident in
+ * one HBM.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are described by star_tensor: a [B, H, S, D] view with element
+ *   strides sB, sH, sS and unit stride along D.  Data must be device memory
+ *   aligned to 16 bytes, and every stride times the element size must be a
+ *   multiple of 16 bytes.
+ * - Q/K/V are bf16 (STAR_BF16); fp32 (STAR_F32) inputs are accepted by
+ *   Phase 1 and Phase 2 and rounded to bf16 (nearest-even) when loaded.
+ * - GQA: query head h reads KV head h / g, g = Hq / Hkv (g <= 16).
+ * - Head dim D is 64 or 128.
+ * - Position ids: a context token's position is its index in the context;
+ *   the KV cache is position-contiguous, so cache index == position.
+ * - lse values are natural-log log-sum-exp of the scaled scores (scale is
+ *   passed by the caller, normally 1/sqrt(D)).  A row that sees no key has
+ *   o = 0 and lse = -inf.
+ * - Ownership: the caller allocates and owns every buffer.  No entry point
+ *   allocates, frees or synchronises.  Work is enqueued on `stream` (a
+ *   hipStream_t passed as void*; NULL = the null stream) and the call returns
+ *   without waiting.  The library holds no mutable global state, so calls
+ *   are reentrant and thread-safe.
+ * - Errors: arguments are validated on the host before anything is
+ *   enqueued; a negative star_status is returned and nothing runs.  A launch
+ *   failure reported by the HIP runtime returns STAR_ERR_HIP.  No C++
+ *   exception crosses this boundary.  Inputs holding NaN or Inf give
+ *   unspecified (but memory-safe) results.
+ */
+#ifndef STAR_ATTN_H
+#define STAR_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STAR_OK = 0,
+  STAR_ERR_NULL = -1,        /* a required pointer is NULL */
+  STAR_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+  STAR_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination */
+  STAR_ERR_ALIGN = -4,       /* data or stride not 16-byte aligned */
+  STAR_ERR_UNSUPPORTED = -5, /* valid request this build does not serve */
+  STAR_ERR_HIP = -6          /* the HIP runtime reported a launch error */
+} star_status;
+
+typedef enum { STAR_BF16 = 0, STAR_F32 = 1 } star_dtype;
+
+/* [B, H, S, D] device tensor; strides in elements; D has unit stride. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* star_dtype */
+  int32_t reserved;
+  int64_t B, H, S, D;
+  int64_t sB, sH, sS;
+} star_tensor;
+
+/* Largest number of KV partitions star_phase2_partial accepts. */
+#define STAR_MAX_PARTS 128
+/* Split chunks of a partition are whole multiples of this many keys. */
+#define STAR_SPLIT_ALIGN 64
+
+/*
+ * Rotary position embedding at original position ids (rotate-half form).
+ * Pair (j, j + D/2) of a row at position p is rotated by the angle
+ * p * theta_j, theta_j = base^(-2j/D): the anchor block keeps the first
+ * block's positions and every token keeps its own (Pith review of Star
+ * Attention, "What carries the argument"; atlas.scime.ai summary, anchor
+ * position-id ablation).  The angle is reduced in fp64 so that it stays
+ * exact to about 1e-7 rad at million-token positions; sin/cos and the
+ * rotation run in fp32; the result is rounded to the output dtype.
+ *
+ *   x_in   [B, H, S, D] bf16 or fp32.
+ *   x_out  same shape and dtype; may alias x_in exactly (in place).
+ *   pos    device int64 [S] position of each row, or NULL for pos0 + s.
+ * Returns STAR_OK or a negative star_status.
+ */
+int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out,
+                    const int64_t* pos, int64_t pos0, double base,
+                    void* stream);
+
+/*
+ * Append new tokens' KV to a position-contiguous cache: the query host
+ * stores the query and generated tokens' KV (Pith review of Star Attention,
+ * "What carries the argument").  Row t of k_new is rotated at position
+ * pos0 + t (when rope != 0) and written to k_cache row slot0 + t; row t of
+ * v_new is copied to v_cache row slot0 + t.
+ *
+ *   k_new, v_new      [B, Hkv, T, D] bf16.
+ *   k_cache, v_cache  [B, Hkv, S, D] bf16, slot0 + T <= S.
+ */
+int star_kv_append(const star_tensor* k_new, const star_tensor* v_new,
+                   const star_tensor* k_cache, const star_tensor* v_cache,
+                   int64_t slot0, int64_t pos0, double base, int32_t rope,
+                   void* stream);
+
+/*
+ * Phase 1: anchor-block blockwise-local causal attention.
+ * The context (length L = q->S) is cut into blocks [i*b, min((i+1)*b, L)).
+ * Rows of the first block attend causally within it.  A row at position p
+ * of block i >= 1 attends to the anchor keys [0, anchor_len) (the first
+ * tokens at their original positions; their K/V are the first block's K/V,
+ * read in place) and to its own block's keys up to and including p.
+ * Anchor rows are never recomputed or output for later blocks (Pith review
+ * of Star Attention, "What carries the argument" and Referee Report minor
+ * comment on Section 2.1; atlas.scime.ai summary, "Approach").
+ * anchor_len = block_b is the method; 0 <= anchor_len < block_b gives the
+ * pages' smaller-anchor and no-anchor ablations.
+ *
+ *   q      [B, Hq, L, D] bf16 or fp32, rotated.
+ *   k, v   [B, Hkv, L, D], same dtype as q, k rotated.
+ *   o      [B, Hq, L, D] bf16 output.
+ *   lse    fp32 [B, Hq, L] contiguous output, or NULL.
+ */
+int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
+                           const star_tensor* v, int64_t block_b,
+                           int64_t anchor_len, float scale,
+                           const star_tensor* o, float* lse, void* stream);
+
+/*
+ * Phase 2 partials: local attention of query rows over each KV partition.
+ * Partition j covers cache rows [part_offsets[j], part_offsets[j+1]); the
+ * last partition is the query host and also holds the query/decode tokens'
+ * KV.  Each partition is cut into `splits` chunks of
+ * c_j = roundup(ceil(n_j / splits), STAR_SPLIT_ALIGN) keys; chunk s covers
+ * [off_j + s*c_j, min(off_j + (s+1)*c_j, off_{j+1})) and may be empty.
+ * Query row r sits at position q_pos0 + r and sees cache row c iff
+ * c <= q_pos0 + r.  For every chunk the call writes the chunk-local
+ * attention output (normalised within the chunk) and its lse: one vector
+ * and one scalar per token (Pith review of Star Attention, "Core claim",
+ * "Circularity Check").
+ *
+ *   q             [B, Hq, Lq, D] bf16 or fp32, rotated.
+ *   k_cache/v_cache [B, Hkv, S, D], same dtype as q.
+ *   part_offsets  host int64 [P + 1], non-decreasing, last <= S.
+ *   o_part        device fp32 [P*splits, B, Hq, Lq, D] contiguous, chunk
+ *                 index j*splits + s.
+ *   lse_part      device fp32 [P*splits, B, Hq, Lq] contiguous.
+ * 1 <= P <= STAR_MAX_PARTS, 1 <= splits <= 1024.
+ */
+int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
+                        const star_tensor* v_cache,
+                        const int64_t* part_offsets, int32_t P, int32_t splits,
+                        int64_t q_pos0, float scale, float* o_part,
+                        float* lse_part, void* stream);
+
+/*
+ * Exact online-softmax (log-sum-exp) merge of N partials per row:
+ * s = log(sum_n exp(s_n)), A = sum_n exp(s_n - s) * A_n; partials with
+ * s_n = -inf carry no weight (Pith review of Star Attention, Referee Report
+ * minor comment on Algorithm 2; "Circularity Check").
+ *
+ *   o_part    fp32 [N, R, D] contiguous, R = o->B * o->H * o->S.
+ *   lse_part  fp32 [N, R] contiguous.
+ *   o         [B, H, S, D] bf16 or fp32 output (row r = (b*H + h)*S + s).
+ *   lse       fp32 [R] contiguous output, or NULL.
+ * 1 <= N <= 65536.
+ */
+int star_lse_merge(const float* o_part, const float* lse_part, int32_t N,
+                   const star_tensor* o, float* lse, void* stream);
+
+/* Human-readable name of a star_status value (static storage). */
+const char* star_status_string(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int star_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STAR_ATTN_H */

@@ -1,0 +1,132 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects invalid arguments before anything is enqueued.
+No call here reaches a kernel launch, so this runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "star_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libstarattn.so not built")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced on the host
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(star_\w+)\s*\(", text, re.M)))
+
+
+def T(B=1, H=2, S=64, D=64, dtype=0, data=FAKE, strides=None):
+    if strides is None:
+        strides = (H * S * D, S * D, D)
+    return _lib.StarTensor(data, dtype, 0, B, H, S, D, *strides)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == set(_lib.EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert lib.star_abi_version() == 100
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.star_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.star_status_string(-99)
+
+
+def p1(lib, q, k, v, o, b=16, a=16, scale=0.125, lse=None):
+    return lib.star_phase1_blocklocal(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), b, a,
+                                      scale, ctypes.byref(o), lse, None)
+
+
+def test_phase1_validation(lib):
+    ok = dict(B=1, H=2, S=64, D=64)
+    q, k, v, o = T(**ok), T(B=1, H=1, S=64, D=64), T(B=1, H=1, S=64, D=64), T(**ok)
+    assert lib.star_phase1_blocklocal(None, ctypes.byref(k), ctypes.byref(v), 16, 16, 0.1,
+                                      ctypes.byref(o), None, None) == -1
+    assert p1(lib, T(**ok, data=0), k, v, o) == -1
+    assert p1(lib, T(**ok, dtype=7), k, v, o) == -3
+    assert p1(lib, q, k, v, T(**ok, dtype=1)) == -3            # O must be bf16
+    assert p1(lib, T(**ok, data=FAKE + 2), k, v, o) == -4
+    assert p1(lib, T(**ok, strides=(8192, 4096, 63)), k, v, o) == -4
+    assert p1(lib, T(B=1, H=2, S=64, D=96), T(B=1, H=1, S=64, D=96),
+              T(B=1, H=1, S=64, D=96), T(B=1, H=2, S=64, D=96)) == -5
+    assert p1(lib, T(B=1, H=3, S=64, D=64), T(B=1, H=2, S=64, D=64),
+              T(B=1, H=2, S=64, D=64), T(B=1, H=3, S=64, D=64)) == -2
+    assert p1(lib, T(B=1, H=32, S=64, D=64), k, v, T(B=1, H=32, S=64, D=64)) == -5  # g > 16
+    assert p1(lib, q, k, v, o, b=0) == -2
+    assert p1(lib, q, k, v, o, b=16, a=17) == -2
+    assert p1(lib, q, k, v, o, a=-1) == -2
+    assert p1(lib, q, k, v, o, scale=float("nan")) == -2
+    assert p1(lib, q, T(B=1, H=1, S=63, D=64), T(B=1, H=1, S=63, D=64), o) == -2
+    assert p1(lib, q, k, v, T(B=1, H=2, S=32, D=64)) == -2
+    assert p1(lib, q, k, v, o, lse=ctypes.c_void_p(FAKE + 1)) == -4
+    # empty context: nothing to do, nothing enqueued
+    z = dict(B=1, S=0, D=64)
+    assert p1(lib, T(H=2, **z), T(H=1, **z), T(H=1, **z), T(H=2, **z)) == 0
+
+
+def p2(lib, q, kc, vc, offs, P=None, splits=1, qpos=0, scale=0.1, op=FAKE, lp=FAKE):
+    P = len(offs) - 1 if P is None else P
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    return lib.star_phase2_partial(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc), arr,
+                                   P, splits, qpos, scale, op, lp, None)
+
+
+def test_phase2_validation(lib):
+    q = T(B=1, H=4, S=3, D=128)
+    kc = T(B=1, H=1, S=100, D=128)
+    vc = T(B=1, H=1, S=100, D=128)
+    assert p2(lib, q, kc, vc, [0, 50, 100], op=None) == -1
+    assert p2(lib, q, kc, vc, [0, 50, 40]) == -2             # non-monotone
+    assert p2(lib, q, kc, vc, [0, 50, 101]) == -2            # past the cache
+    assert p2(lib, q, kc, vc, [-1, 50, 100]) == -2
+    assert p2(lib, q, kc, vc, [0, 100], splits=0) == -2
+    assert p2(lib, q, kc, vc, [0, 100], splits=1025) == -2
+    assert p2(lib, q, kc, vc, list(range(0, 130)), P=129) == -2
+    assert p2(lib, q, kc, vc, [0, 100], qpos=-1) == -2
+    assert p2(lib, q, kc, vc, [0, 100], op=FAKE + 4) == -4
+    assert p2(lib, q, T(B=1, H=1, S=100, D=128, dtype=1), vc, [0, 100]) == -3
+    assert p2(lib, T(B=1, H=4, S=0, D=128), kc, vc, [0, 100]) == 0
+
+
+def test_merge_rope_append_validation(lib):
+    o = T(B=1, H=2, S=4, D=64)
+    m = lambda n, oo=o, op=FAKE, lp=FAKE: lib.star_lse_merge(op, lp, n, ctypes.byref(oo), None, None)
+    assert m(1, op=None) == -1
+    assert m(0) == -2
+    assert m(70000) == -2
+    assert m(2, oo=T(B=1, H=2, S=4, D=80)) == -5
+    assert m(2, op=FAKE + 8) == -4
+    assert m(2, oo=T(B=1, H=2, S=0, D=64)) == 0
+    x = T(B=1, H=2, S=8, D=128)
+    r = lambda a, b, pos=None, pos0=0, base=5e5: lib.star_rope_apply(
+        ctypes.byref(a), ctypes.byref(b), pos, pos0, base, None)
+    assert r(x, T(B=1, H=2, S=8, D=128, dtype=1)) == -3
+    assert r(x, T(B=1, H=2, S=9, D=128)) == -2
+    assert r(T(B=1, H=2, S=8, D=72), T(B=1, H=2, S=8, D=72)) == -5
+    assert r(x, x, base=1.0) == -2
+    assert r(x, x, pos0=-3) == -2
+    assert r(T(B=1, H=2, S=0, D=128), T(B=1, H=2, S=0, D=128)) == 0
+    kn, vn = T(B=1, H=2, S=3, D=128), T(B=1, H=2, S=3, D=128)
+    kc, vc = T(B=1, H=2, S=10, D=128), T(B=1, H=2, S=10, D=128)
+    a = lambda slot, kk=kc: lib.star_kv_append(ctypes.byref(kn), ctypes.byref(vn),
+                                               ctypes.byref(kk), ctypes.byref(vc), slot, 5,
+                                               5e5, 1, None)
+    assert a(8) == -2
+    assert a(-1) == -2
+    assert a(0, kk=T(B=1, H=2, S=11, D=128)) == -2

@@ -1,0 +1,172 @@
+"""GPU parity on small shapes: every entry point of the C ABI against the CPU
+oracle, element by element, including ragged tails, anchor variants, GQA
+ratios, empty chunks and fully masked rows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_amd as sa
+import oracle.star_oracle as so
+from gpu_util import (check_lse, check_out, chunk_ranges, f64, host64, rand_tensor,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(seed, B, Hq, Hkv, L, D, bf16=True, scale=1.0):
+    q = rand_tensor(seed, 0, B, Hq, L, D, scale, bf16)
+    k = rand_tensor(seed, 1, B, Hkv, L, D, scale, bf16)
+    v = rand_tensor(seed, 2, B, Hkv, L, D, scale, bf16)
+    return q, k, v
+
+
+P1_CASES = [
+    # B, Hq, Hkv, D, L, b, a, bf16, scale
+    (1, 2, 1, 64, 512, 128, 128, True, 0.125),     # tiny workload, bf16
+    (1, 2, 1, 64, 512, 128, 128, False, 0.125),    # tiny workload, fp32 inputs
+    (2, 8, 2, 128, 700, 200, 200, True, 1.0),      # ragged tail, b % 64 != 0
+    (1, 4, 1, 128, 333, 1000, 1000, True, 1.0),    # single block (b >= L)
+    (1, 8, 1, 128, 640, 128, 0, True, 1.0),        # no anchor (block-diagonal)
+    (1, 4, 4, 64, 600, 256, 100, True, 1.0),       # smaller anchor, MHA
+    (1, 16, 1, 128, 300, 128, 128, True, 1.0),     # g = 16
+    (1, 24, 8, 128, 300, 100, 100, True, 1.0),     # g = 3
+    (1, 5, 5, 64, 97, 32, 32, True, 1.0),          # L < one key tile
+    (1, 8, 2, 128, 1, 16, 16, True, 1.0),          # one token
+]
+
+
+@pytest.mark.parametrize("case", P1_CASES, ids=[str(i) for i in range(len(P1_CASES))])
+def test_phase1_parity(case):
+    B, Hq, Hkv, D, L, b, a, bf16, sc = case
+    print(f"phase1 case {case}", flush=True)
+    q, k, v = _qkv(11, B, Hq, Hkv, L, D, bf16, sc)
+    scale = 1 / math.sqrt(D)
+    o, lse = sa.phase1_blocklocal(to_dev(q), to_dev(k), to_dev(v), b, a, want_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = so.phase1(f64(q), f64(k), f64(v), b, a if b < L else 0, scale)
+    check_out(host64(o), ref_o, "O")
+    check_lse(host64(lse), ref_l, "LSE")
+
+
+P2_CASES = [
+    # B, Hq, Hkv, D, L, Lq, b, splits
+    (1, 2, 1, 64, 512, 16, 128, 1),     # tiny workload query phase (flash path)
+    (1, 2, 1, 64, 512, 16, 128, 3),
+    (1, 32, 8, 128, 1000, 64, 300, 2),  # flash path, ragged partitions
+    (2, 8, 2, 128, 777, 1, 200, 4),     # decode path (g*Lq = 4)
+    (1, 16, 2, 128, 500, 2, 128, 3),    # decode path, g*Lq = 16
+    (1, 4, 1, 64, 300, 1, 100, 8),      # decode path, D = 64, empty chunks
+    (1, 24, 8, 128, 400, 5, 90, 2),     # decode path, g = 3, Lq = 5
+    (1, 8, 1, 128, 300, 3, 64, 16),     # flash path (g*Lq = 24), many empty chunks
+]
+
+
+@pytest.mark.parametrize("case", P2_CASES, ids=[str(i) for i in range(len(P2_CASES))])
+def test_phase2_partials_and_merge(case):
+    B, Hq, Hkv, D, L, Lq, b, splits = case
+    print(f"phase2 case {case}", flush=True)
+    g = Hq // Hkv
+    N = L + Lq
+    q = rand_tensor(21, 3, B, Hq, Lq, D)
+    kc = rand_tensor(21, 4, B, Hkv, N + 7, D)   # spare rows past the cache end
+    vc = rand_tensor(21, 5, B, Hkv, N + 7, D)
+    parts = so.partitions(L, b, N)
+    offs = [p[0] for p in parts] + [parts[-1][1]]
+    scale = 1 / math.sqrt(D)
+    op, lp = sa.phase2_partial(to_dev(q), to_dev(kc), to_dev(vc), offs, splits, q_pos0=L)
+    o, l = sa.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    ranges = chunk_ranges(offs, splits)
+    assert len(ranges) == op.shape[0]
+    qf, kf, vf = f64(q), f64(kc), f64(vc)
+    qpos = L + np.arange(Lq)
+    ref_op = np.zeros(op.shape)
+    ref_lp = np.zeros(lp.shape)
+    ref_o = np.zeros(o.shape)
+    ref_l = np.zeros(l.shape)
+    for bb in range(B):
+        for h in range(Hq):
+            for c, (k0, k1) in enumerate(ranges):
+                ro, rl = so.partial(qf[bb, h], qpos, kf[bb, h // g], vf[bb, h // g], k0, k1, scale)
+                ref_op[c, bb, h], ref_lp[c, bb, h] = ro, rl
+            ro, rl, _, _ = so.phase2(qf[bb, h], qpos, kf[bb, h // g], vf[bb, h // g], parts, scale)
+            ref_o[bb, h], ref_l[bb, h] = ro, rl
+    check_out(host64(op), ref_op, "o_part")
+    check_lse(host64(lp), ref_lp, "lse_part")
+    check_out(host64(o), ref_o, "O merged")
+    check_lse(host64(l), ref_l, "LSE merged")
+
+
+@pytest.mark.parametrize("N,D,out_bf16", [(4, 64, False), (37, 128, True), (300, 128, False)])
+def test_merge_parity(N, D, out_bf16):
+    """Merge partials the oracle produced (random key ranges, some empty)."""
+    rng = np.random.default_rng(N)
+    B, H, S, M = 1, 3, 5, 200
+    q = rng.standard_normal((B, H, S, D))
+    k = rng.standard_normal((M, D))
+    v = rng.standard_normal((M, D))
+    cuts = np.sort(rng.integers(0, M + 1, size=N - 1))
+    bounds = [0, *cuts.tolist(), M]
+    op = np.zeros((N, B, H, S, D))
+    lp = np.zeros((N, B, H, S))
+    for n in range(N):
+        for h in range(H):
+            o, l = so.attend(q[0, h], k[bounds[n]:bounds[n + 1]], v[bounds[n]:bounds[n + 1]],
+                             np.ones((S, bounds[n + 1] - bounds[n]), bool), 1 / math.sqrt(D))
+            op[n, 0, h], lp[n, 0, h] = o, l
+    ref_o, ref_l = so.lse_merge(op, lp)
+    o, l = sa.lse_merge(torch.from_numpy(op.astype(np.float32)).cuda(),
+                        torch.from_numpy(lp.astype(np.float32)).cuda(),
+                        out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    check_out(host64(o), ref_o, "merged O")
+    check_lse(host64(l), ref_l, "merged LSE")
+
+
+@pytest.mark.parametrize("D,f32,pos0", [(128, False, 0), (128, False, 131000),
+                                        (64, True, 1048000), (128, True, 1048570)])
+def test_rope_parity(D, f32, pos0):
+    B, H, S = 2, 3, 67
+    x = rand_tensor(31, 0, B, H, S, D, bf16=not f32)
+    xd = to_dev(x)
+    out = sa.rope_apply(xd.clone(), pos0=pos0, base=500000.0)
+    pos = torch.arange(pos0, pos0 + S, dtype=torch.int64, device="cuda")
+    out2 = torch.empty_like(xd)
+    sa.rope_apply(xd, pos=pos, base=500000.0, out=out2)
+    torch.cuda.synchronize()
+    ref = so.rope(f64(x), np.arange(pos0, pos0 + S), 500000.0)
+    for got in (host64(out), host64(out2)):
+        err = np.abs(got - ref)
+        if f32:
+            assert err.max() < 2e-5, err.max()
+        else:  # bf16 rounding of the result: half an ulp, relative 2^-8
+            assert (err <= np.abs(ref) * 2.0**-8 + 1e-5).all(), err.max()
+
+
+def test_rope_angle_precision_at_1m():
+    """Unit pairs rotated at positions near 2^20: the fp32 result must sit
+    within ~1e-6 of (cos, sin) of the exact angle."""
+    D, S, pos0 = 128, 64, 1048576 - 64
+    x = np.zeros((1, 1, S, D), np.float32)
+    x[..., : D // 2] = 1.0
+    out = sa.rope_apply(to_dev(x), pos0=pos0, base=500000.0)
+    torch.cuda.synchronize()
+    ref = so.rope(x.astype(np.float64), np.arange(pos0, pos0 + S), 500000.0)
+    assert np.abs(host64(out) - ref).max() < 2e-6
+
+
+def test_kv_append_parity():
+    B, H, T, D, S = 2, 4, 5, 128, 40
+    kn = rand_tensor(41, 7, B, H, T, D)
+    vn = rand_tensor(41, 8, B, H, T, D)
+    kc = torch.zeros((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    sa.kv_append(to_dev(kn), to_dev(vn), kc, vc, slot0=30, pos0=123456, base=500000.0)
+    torch.cuda.synchronize()
+    ref_k = so.rope(f64(kn), 123456 + np.arange(T), 500000.0)
+    got_k = host64(kc)[:, :, 30:35]
+    assert (np.abs(got_k - ref_k) <= np.abs(ref_k) * 2.0**-8 + 1e-5).all()
+    assert np.array_equal(host64(vc)[:, :, 30:35], f64(vn))
+    assert (host64(kc)[:, :, :30] == 0).all() and (host64(kc)[:, :, 35:] == 0).all()
