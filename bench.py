@@ -1,0 +1,223 @@
+"""Benchmark of the Star Attention two-phase hot path on one MI355X.
+
+One step = one whole pass over one batch of synthetic input, resident in HBM:
+RoPE of the context Q/K at original positions (K straight into the KV cache),
+Phase-1 anchor-block blockwise-local attention, the Phase-2 query (RoPE, KV
+append, partials over every partition, LSE merge) and every decode step
+(same, one token each).  Default workload: Llama-3.1-8B layer shapes at
+131072-token context, b = 16384 (8 KV partitions), 64 query tokens, 128
+decode steps.
+
+Prints ONE JSON line.  ``value`` is whole-step context tokens/s
+(B*L per step / step time).  ``phase1`` / ``decode`` hold the per-phase
+rates; ``roofline`` is for the dominant kernel (the Phase-1 flash kernel,
+bf16 MFMA), timed with HIP events on the stream it is launched on;
+``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Phase1 context tokens/s + TFLOP/s; Phase2 decode GB/s (8B shapes, 128K ctx)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "phase1_flash_llama8b-128k_pmc.txt")
+FLASH_SRC = os.path.join(ROOT, "block_sparse_amd", "csrc", "flash.hip")
+
+
+def phase1_pairs(L: int, b: int, a: int) -> int:
+    """Useful (query, key) pairs of Phase 1 per head: block 1 is causal over
+    itself; block i >= 2 sees a anchor keys plus its causal prefix."""
+    tot = 0
+    for i, s in enumerate(range(0, L, b)):
+        n = min(s + b, L) - s
+        tot += n * (n + 1) // 2 + (a * n if i > 0 else 0)
+    return tot
+
+
+def phase1_flops(w) -> float:
+    return 4.0 * w.D * w.Hq * w.B * phase1_pairs(w.L, w.b, w.a)
+
+
+def decode_bytes(w, t: int) -> int:
+    """K and V bytes a decode step must read: every visible cached token."""
+    return (w.L + w.Lq + t + 1) * w.Hkv * w.B * w.D * 2 * 2
+
+
+def pmc_traffic():
+    """HBM traffic per Phase-1 launch from the committed rocprofv3 counter
+    summary, or None when it is absent or the kernel source changed since."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"flash_src_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t:
+        return None
+    cur = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
+    return float(t.group(1)) if m.group(1) == cur else None
+
+
+def cpu_baseline(w, x):
+    """Time the CPU oracle (as it stands) on a bounded sample of Phase 1:
+    the last ``rows`` rows of block 2 of query head 0, batch 0 (anchor plus
+    a long causal prefix).  Scaled to whole-workload context tokens/s by the
+    ratio of useful (query, key) pairs."""
+    import numpy as np
+
+    import oracle.star_oracle as so
+    from workloads import as_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    scale = 1.0 / math.sqrt(w.D)
+    blk = 1 if w.L > w.b else 0
+    s = blk * w.b
+    e = min(s + w.b, w.L)
+    rows = min(4096, e - s)
+    pos = np.arange(e - rows, e)
+    t0 = time.perf_counter()
+    kv = 0
+    K = so.rope(as_f64(x["k"][0, kv]), np.arange(w.L), w.base) if w.rope else as_f64(x["k"][0, kv])
+    V = as_f64(x["v"][0, kv])
+    q = as_f64(x["q"][0, 0][pos])
+    q = so.rope(q, pos, w.base) if w.rope else q
+    so.phase1_rows(q, pos, K, V, w.b, w.a, scale)
+    dt = time.perf_counter() - t0
+    sample_pairs = sum((w.a if blk > 0 else 0) + (p - s + 1) for p in pos)
+    total_pairs = phase1_pairs(w.L, w.b, w.a) * w.Hq * w.B
+    tokens_per_s = w.B * w.L / (dt * total_pairs / sample_pairs)
+    return {"value": tokens_per_s, "unit": "context tokens/s (Phase 1, extrapolated)",
+            "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, Phase 1 of {rows} rows (positions {pos[0]}-{pos[-1]}, "
+                       f"block {blk + 1}) of one query head, incl. RoPE of that KV head; "
+                       f"{dt:.1f} s; scaled by useful (q,k) pairs {sample_pairs:.3e} of "
+                       f"{total_pairs:.3e}")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b-128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phase1-only", action="store_true",
+                    help="time only RoPE + Phase 1 (for counter runs)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of this many MiB first "
+                         "(reference kernel for rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_amd.pipeline import StarAttentionStep
+    from workloads import WORKLOADS, inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    x = inputs(w, as_bf16=True)
+    dev = {n: torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).cuda() for n, t in x.items()}
+    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, w.Lq, w.T, rope=w.rope, base=w.base)
+    st.load_context(dev["v"])
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rec=None):
+        if rec is not None:
+            rec["p1"][0].record()
+        st.rope_context(dev["q"], dev["k"])
+        if rec is not None:
+            rec["p1"][1].record()
+        st.phase1()
+        if rec is not None:
+            rec["p1"][2].record()
+        if args.phase1_only:
+            return
+        st.query(dev["qq"], dev["kq"], dev["vq"])
+        if rec is not None:
+            rec["dec"][0].record()
+        for t in range(w.T):
+            st.decode(t, dev["qd"][:, :, t:t + 1], dev["kd"][:, :, t:t + 1],
+                      dev["vd"][:, :, t:t + 1])
+        if rec is not None:
+            rec["dec"][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = [{"p1": [ev(), ev(), ev()], "dec": [ev(), ev()]} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in recs:
+        step(r)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms_step = total * 1e3 / args.steps
+
+    rope_ms = np.mean([r["p1"][0].elapsed_time(r["p1"][1]) for r in recs])
+    p1_ms = np.mean([r["p1"][1].elapsed_time(r["p1"][2]) for r in recs])
+    flops = phase1_flops(w)
+    p1_tflops = flops / (p1_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": w.B * w.L * args.steps / total,
+        "unit": "context tokens/s (whole two-phase step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "context": w.L, "block": w.b, "anchor": w.a,
+                   "query_tokens": w.Lq, "decode_steps": w.T, "rope_base": w.base,
+                   "splits_query": st.sq, "splits_decode": st.sd,
+                   "phase1_only": bool(args.phase1_only)},
+        "phase1": {"kernel_ms": p1_ms, "rope_ms": rope_ms,
+                   "context_tokens_per_s": w.B * w.L / (p1_ms * 1e-3),
+                   "context_tokens_per_s_with_rope": w.B * w.L / ((p1_ms + rope_ms) * 1e-3),
+                   "tflops": p1_tflops, "algorithmic_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": pmc_traffic(),
+                     "kernel": "flash_kernel (Phase 1)"},
+    }
+    if not args.phase1_only and w.T > 0:
+        dec_ms = np.mean([r["dec"][0].elapsed_time(r["dec"][1]) for r in recs])
+        byts = sum(decode_bytes(w, t) for t in range(w.T))
+        out["decode"] = {"us_per_step": dec_ms * 1e3 / w.T,
+                         "gbps": byts / (dec_ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": byts / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "note": "whole decode step (RoPE, KV append, partials, merge), "
+                                 "K+V bytes of every visible token"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -158,6 +158,9 @@ def lse_merge(o_part, lse_part, out=None, lse=None, out_dtype=torch.float32,
         out = torch.empty((B, H, S, D), dtype=out_dtype, device=o_part.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=o_part.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * H * S):
+        raise ValueError("lse must be a contiguous fp32 tensor of B*H*S rows")
     do = _desc(out)
     st = library().star_lse_merge(_ptr(o_part), _ptr(lse_part), int(N), ctypes.byref(do),
                                   _ptr(lse), _stream(o_part))

@@ -1,0 +1,135 @@
+"""Host-side driver of one pass of the two-phase hot path for one layer.
+
+It owns the device buffers (allocated once, resident in HBM) and issues the
+library calls in the order the method runs them (Star Attention, pith
+review "What carries the argument"; atlas.scime.ai summary "Approach"):
+
+  Phase 1  rope(Q) and rope(K) at original positions (K straight into the
+           position-contiguous KV cache), then block-local attention with
+           the anchor.  The anchor's KV is never copied: it is block 1's KV
+           in the cache, so after Phase 1 the cache holds exactly L entries.
+  Phase 2  query tokens: rope(q) at L.., append their K/V to the last
+           partition (the query host), partials over every partition and
+           the LSE merge.  Then each generated token repeats the same with
+           one row, attending to everything cached so far.
+
+All buffers are caller-visible torch tensors; every computation runs in the
+library's kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import kv_append, lse_merge, phase1_blocklocal, phase2_partial, rope_apply
+
+
+def partition_offsets(L: int, b: int, cache_len: int):
+    """Partition j = block j's cache rows; the last one extends to cache_len."""
+    offs = list(range(0, L, b)) + [cache_len]
+    return offs
+
+
+def choose_splits(B: int, Hkv: int, P: int, part_len: int, target_wg: int,
+                  min_chunk: int) -> int:
+    """Chunks per partition so that B*Hkv*P*splits workgroups fill the chip
+    without cutting chunks below ``min_chunk`` keys."""
+    want = max(1, math.ceil(target_wg / max(1, B * Hkv * P)))
+    cap = max(1, math.ceil(part_len / min_chunk))
+    return int(min(want, cap, 1024))
+
+
+class StarAttentionStep:
+    """Buffers and call sequence of one Star Attention layer pass."""
+
+    def __init__(self, B, Hq, Hkv, D, L, b, Lq, T, anchor=None, rope=True,
+                 base=500000.0, device="cuda", want_lse=True,
+                 splits_query=None, splits_decode=None):
+        self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
+        self.L, self.b, self.Lq, self.T = L, b, Lq, T
+        self.a = b if anchor is None else anchor
+        self.rope, self.base = rope, base
+        self.scale = 1.0 / math.sqrt(D)
+        bf = torch.bfloat16
+        S = L + Lq + T
+        self.S = S
+        dev = torch.device(device)
+        self.qr = torch.empty((B, Hq, L, D), dtype=bf, device=dev)
+        self.kc = torch.empty((B, Hkv, S, D), dtype=bf, device=dev)
+        self.vc = torch.empty((B, Hkv, S, D), dtype=bf, device=dev)
+        self.o1 = torch.empty((B, Hq, L, D), dtype=bf, device=dev)
+        self.lse1 = torch.empty((B, Hq, L), dtype=torch.float32, device=dev) if want_lse else None
+        self.qq_r = torch.empty((B, Hq, max(Lq, 1), D), dtype=bf, device=dev)
+        self.qd_r = torch.empty((B, Hq, max(T, 1), D), dtype=bf, device=dev)
+        self.o2 = torch.empty((B, Hq, Lq, D), dtype=torch.float32, device=dev)
+        self.lse2 = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
+        self.od = torch.empty((B, Hq, max(T, 1), D), dtype=torch.float32, device=dev)
+        self.lsed = torch.empty((max(T, 1), B, Hq), dtype=torch.float32, device=dev)
+        self.P = -(-L // b)
+        part_len = min(b, L)
+        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 512, 512)
+        self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 1536, 256)
+        nq = self.P * self.sq
+        nd = self.P * self.sd
+        self.op_q = torch.empty((nq, B, Hq, max(Lq, 1), D), dtype=torch.float32, device=dev)
+        self.lp_q = torch.empty((nq, B, Hq, max(Lq, 1)), dtype=torch.float32, device=dev)
+        self.op_d = torch.empty((nd, B, Hq, 1, D), dtype=torch.float32, device=dev)
+        self.lp_d = torch.empty((nd, B, Hq, 1), dtype=torch.float32, device=dev)
+
+    # -- inputs -----------------------------------------------------------
+    def load_context(self, v):
+        """Place the context V in the cache (V needs no rotation)."""
+        self.vc[:, :, :self.L].copy_(v)
+
+    # -- phases -----------------------------------------------------------
+    def rope_context(self, q, k):
+        L = self.L
+        if self.rope:
+            rope_apply(q, pos0=0, base=self.base, out=self.qr)
+            rope_apply(k, pos0=0, base=self.base, out=self.kc[:, :, :L])
+        else:
+            self.qr.copy_(q)
+            self.kc[:, :, :L].copy_(k)
+
+    def phase1(self):
+        L = self.L
+        phase1_blocklocal(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
+                          self.scale, out=self.o1, lse=self.lse1)
+
+    def query(self, qq, kq, vq):
+        L, Lq = self.L, self.Lq
+        if Lq == 0:
+            return
+        if self.rope:
+            rope_apply(qq, pos0=L, base=self.base, out=self.qq_r[:, :, :Lq])
+        else:
+            self.qq_r[:, :, :Lq].copy_(qq)
+        kv_append(kq, vq, self.kc, self.vc, slot0=L, pos0=L, base=self.base, rope=self.rope)
+        offs = partition_offsets(L, self.b, L + Lq)
+        op, lp = phase2_partial(self.qq_r[:, :, :Lq], self.kc, self.vc, offs, self.sq,
+                                q_pos0=L, scale=self.scale,
+                                o_part=self.op_q, lse_part=self.lp_q)
+        lse_merge(op, lp, out=self.o2, lse=self.lse2)
+
+    def decode(self, t, qd, kd, vd):
+        """Generated token t (inputs are views [B, H, 1, D])."""
+        pos = self.L + self.Lq + t
+        qv = self.qd_r[:, :, t:t + 1]
+        if self.rope:
+            rope_apply(qd, pos0=pos, base=self.base, out=qv)
+        else:
+            qv.copy_(qd)
+        kv_append(kd, vd, self.kc, self.vc, slot0=pos, pos0=pos, base=self.base, rope=self.rope)
+        offs = partition_offsets(self.L, self.b, pos + 1)
+        phase2_partial(qv, self.kc, self.vc, offs, self.sd, q_pos0=pos, scale=self.scale,
+                       o_part=self.op_d, lse_part=self.lp_d)
+        lse_merge(self.op_d, self.lp_d, out=self.od[:, :, t:t + 1], lse=self.lsed[t])
+
+    def run(self, q, k, qq, kq, vq, qd, kd, vd):
+        """One whole pass: Phase 1, the query, then every decode step."""
+        self.rope_context(q, k)
+        self.phase1()
+        self.query(qq, kq, vq)
+        for t in range(self.T):
+            self.decode(t, qd[:, :, t:t + 1], kd[:, :, t:t + 1], vd[:, :, t:t + 1])

@@ -120,7 +120,7 @@ def blocks(L: int, b: int):
     return [(s, min(s + b, L)) for s in range(0, L, b)]
 
 
-def phase1_block_keys(i: int, L: int, b: int, a: int):
+def phase1_block_keys(i: int, L: int, b: int, a: int, rows=None):
     """Key ids and explicit mask of the augmented block c'_i (0-based i).
 
     c'_1 = c_1 is plain causal attention over b tokens ([SA-pith] "Referee
@@ -128,16 +128,18 @@ def phase1_block_keys(i: int, L: int, b: int, a: int):
     the anchor).  For i >= 1 the augmented block is [anchor ; c_i]: every row
     sees all ``a`` anchor tokens (the first ``a`` context tokens at their
     original positions) plus its own block's tokens up to itself.
-    Returns (key_ids[m], mask[n_i, m]).
+    Returns (key_ids[m], mask[n, m]); ``rows`` (indices inside the block)
+    selects which mask rows to build, default all n_i rows.
     """
     s, e = blocks(L, b)[i]
     n = e - s
     own = np.arange(s, e)
-    causal = np.tril(np.ones((n, n), dtype=bool))
+    r = np.arange(n) if rows is None else np.asarray(rows)
+    causal = own[None, :] - s <= r[:, None]
     if i == 0:
         return own, causal
     anc = np.arange(0, min(a, L))
-    mask = np.concatenate([np.ones((n, anc.size), dtype=bool), causal], axis=1)
+    mask = np.concatenate([np.ones((r.size, anc.size), dtype=bool), causal], axis=1)
     return np.concatenate([anc, own]), mask
 
 
@@ -179,8 +181,8 @@ def phase1_rows(q_rows, pos, K, V, b: int, a: int, scale: float):
         sel = np.nonzero((pos >= s) & (pos < e))[0]
         if sel.size == 0:
             continue
-        keys, mask = phase1_block_keys(i, L, b, a)
-        oo, ll = attend(q_rows[sel], K[keys], V[keys], mask[pos[sel] - s], scale)
+        keys, mask = phase1_block_keys(i, L, b, a, rows=pos[sel] - s)
+        oo, ll = attend(q_rows[sel], K[keys], V[keys], mask, scale)
         o[sel], lse[sel] = oo, ll
     return o, lse
 

@@ -1,0 +1,130 @@
+"""GPU parity on the five workloads at their full sizes, run through the same
+call sequence the benchmark times (block_sparse_amd.pipeline).
+
+Tiny is compared on every output element, in both its fp32 and bf16 forms.
+The Llama-shaped workloads are compared on outputs the oracle computes one
+by one from the raw seeded inputs:
+  * Phase 1: for the checked KV heads (every query head of their GQA group),
+    the first two and last two rows of every block plus seeded random rows
+    of every block; for llama8b-16k every row of those heads;
+  * Phase 2: every query row and every decode step of the checked heads;
+and on properties that hold at any size (every Phase-1 output and lse of
+every head finite).
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_amd as sa
+import oracle.star_oracle as so
+from block_sparse_amd.pipeline import StarAttentionStep, partition_offsets
+from gpu_util import check_lse, check_out, chunk_ranges, f64, host64, to_dev
+from workloads import TINY, WORKLOADS, as_f64, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "fp32"])
+def test_tiny_full(bf16):
+    w = TINY
+    log(f"tiny bf16={bf16}: inputs")
+    x = inputs(w, as_bf16=bf16)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    o1, l1 = sa.phase1_blocklocal(q, k, v, w.b, w.a, want_lse=True)
+    kc = torch.cat([k, to_dev(x["kq"])], dim=2).contiguous()
+    vc = torch.cat([v, to_dev(x["vq"])], dim=2).contiguous()
+    offs = partition_offsets(w.L, w.b, w.L + w.Lq)
+    op, lp = sa.phase2_partial(to_dev(x["qq"]), kc, vc, offs, splits=1, q_pos0=w.L)
+    o2, l2 = sa.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    ref = so.star_attention(w, {n: as_f64(t) for n, t in x.items()})
+    check_out(host64(o1), ref["O1"], "phase1 O")
+    check_lse(host64(l1), ref["LSE1"], "phase1 LSE")
+    check_out(host64(op), ref["P2o"], "phase2 partials")
+    check_lse(host64(lp), ref["P2l"], "phase2 partial lse")
+    check_out(host64(o2), ref["O2"], "phase2 O")
+    check_lse(host64(l2), ref["LSE2"], "phase2 LSE")
+
+
+# name -> (checked KV heads, random rows per block, full Phase-1 rows?)
+LLAMA = {
+    "llama8b-16k": ((0, 7), 0, True),
+    "llama8b-128k": ((0, 3, 7), 24, False),
+    "llama70b-64k": ((0, 7), 24, False),
+    "llama8b-1m": ((0, 5), 12, False),
+}
+
+
+def sample_rows(w, rows_per_block, seed):
+    rng = np.random.default_rng(seed)
+    pos = []
+    for s, e in so.blocks(w.L, w.b):
+        n = e - s
+        pos += [s, s + 1, e - 2, e - 1]
+        if rows_per_block:
+            pos += (s + rng.choice(n, size=min(rows_per_block, n), replace=False)).tolist()
+    return np.unique(np.array(pos, dtype=np.int64))
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("name", list(LLAMA))
+def test_llama_workload(name):
+    w = WORKLOADS[name]
+    kv_heads, rows_per_block, full_rows = LLAMA[name]
+    g = w.g
+    scale = 1.0 / math.sqrt(w.D)
+    log(f"{name}: generating inputs")
+    x = inputs(w, as_bf16=True)
+    log(f"{name}: GPU pass")
+    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, w.Lq, w.T, rope=True, base=w.base)
+    dev = {n: to_dev(t) for n, t in x.items() if n != "v"}
+    st.load_context(to_dev(x["v"]))
+    st.run(dev["q"], dev["k"], dev["qq"], dev["kq"], dev["vq"], dev["qd"], dev["kd"], dev["vd"])
+    torch.cuda.synchronize()
+    # properties over every head at full size
+    assert bool(torch.isfinite(st.o1).all()), "non-finite Phase-1 output"
+    assert bool(torch.isfinite(st.lse1).all()), "non-finite Phase-1 lse"
+    assert bool(torch.isfinite(st.o2).all()) and bool(torch.isfinite(st.od).all())
+    del dev
+    pos = np.arange(w.L) if full_rows else sample_rows(w, rows_per_block, w.seed)
+    pos_t = torch.from_numpy(pos).cuda()
+    pos_q = w.L + np.arange(w.Lq)
+    pos_d = w.L + w.Lq + np.arange(w.T)
+    worst = {}
+    for bb in range(w.B):
+        for kvh in kv_heads:
+            log(f"{name}: oracle b={bb} kv head {kvh}")
+            K = so.rope(f64(x["k"][bb, kvh]), np.arange(w.L), w.base)
+            V = f64(x["v"][bb, kvh])
+            Kc = np.concatenate([K, so.rope(f64(x["kq"][bb, kvh]), pos_q, w.base),
+                                 so.rope(f64(x["kd"][bb, kvh]), pos_d, w.base)])
+            Vc = np.concatenate([V, f64(x["vq"][bb, kvh]), f64(x["vd"][bb, kvh])])
+            parts = so.partitions(w.L, w.b, w.cache_len)
+            for h in range(kvh * g, (kvh + 1) * g):
+                qrows = so.rope(f64(x["q"][bb, h][pos]), pos, w.base)
+                ro, rl = so.phase1_rows(qrows, pos, K, V, w.b, w.a, scale)
+                go = host64(st.o1[bb, h].index_select(0, pos_t))
+                gl = host64(st.lse1[bb, h].index_select(0, pos_t))
+                e1 = check_out(go, ro, f"{name} phase1 O b{bb} h{h}")
+                e2 = check_lse(gl, rl, f"{name} phase1 LSE b{bb} h{h}")
+                # query rows and every decode step, against global attention
+                qq = so.rope(f64(x["qq"][bb, h]), pos_q, w.base)
+                qd = so.rope(f64(x["qd"][bb, h]), pos_d, w.base)
+                rows = np.concatenate([qq, qd])
+                rpos = np.concatenate([pos_q, pos_d])
+                o, l, _, _ = so.phase2(rows, rpos, Kc, Vc, parts, scale)
+                e3 = check_out(host64(st.o2[bb, h]), o[:w.Lq], f"{name} query O b{bb} h{h}")
+                e4 = check_lse(host64(st.lse2[bb, h]), l[:w.Lq], f"{name} query LSE b{bb} h{h}")
+                e5 = check_out(host64(st.od[bb, h, :w.T]), o[w.Lq:], f"{name} decode O b{bb} h{h}")
+                e6 = check_lse(host64(st.lsed[:w.T, bb, h]), l[w.Lq:], f"{name} decode LSE b{bb} h{h}")
+                for key, val in zip(("p1O", "p1L", "qO", "qL", "dO", "dL"),
+                                    (e1[0], e2, e3[0], e4, e5[0], e6)):
+                    worst[key] = max(worst.get(key, 0.0), val)
+    log(f"{name}: worst max-abs errors {worst} over {pos.size} rows/head")
