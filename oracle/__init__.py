@@ -6,5 +6,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
 from .star_oracle import (  # noqa: F401
     NEG_INF, attend, blocks, dense_causal, kv_cache_entries, lse_merge,
     partial, partitions, phase1, phase1_block_keys, phase1_rows, phase2,
-    rope, rope_theta, star_attention,
+    rope, rope_theta, round_bf16, star_attention,
 )

@@ -75,6 +75,24 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned
+    as float64.  bfloat16 keeps 8 significant bits: with x = m * 2^e,
+    0.5 <= |m| < 1, the result is rint(m * 2^8) * 2^(e-8) (numpy's rint
+    rounds half to even).  Exponents below bfloat16's normal range keep the
+    subnormal quantum 2^-133.
+
+    Rotated Q/K are stored in the model's bfloat16 dtype (the KV cache
+    dtype) before attention reads them ([SA-repo] README: HuggingFace
+    Transformers LLMs; the attention inputs are bf16), so the oracle rounds
+    its exact rotation here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+
+
 # ----------------------------------------------------------------------------
 # masked softmax attention: the one primitive every step uses
 # ----------------------------------------------------------------------------
@@ -270,17 +288,23 @@ def dense_causal(Q, K, V, scale: float):
 # ----------------------------------------------------------------------------
 # the whole hot path on one workload (small workloads only)
 # ----------------------------------------------------------------------------
-def star_attention(w, x: dict, splits_ranges=None):
+def star_attention(w, x: dict, store_bf16: bool = True):
     """Run both phases on a workload's inputs (see ``workloads.inputs``).
 
-    ``x`` maps names to float64 arrays.  Returns a dict with the rotated
+    ``x`` maps names to float64 arrays.  With ``store_bf16`` the rotated
+    Q/K are rounded to bfloat16, the dtype the model stores them in, before
+    attention (see :func:`round_bf16`).  Returns a dict with the rotated
     tensors, Phase-1 O/LSE, the query-phase partials and merged output, and
     one merged output per decode step.
     """
     B, Hq, Hkv, D, L = w.B, w.Hq, w.Hkv, w.D, w.L
     g = Hq // Hkv
     scale = 1.0 / math.sqrt(D)
-    rot = (lambda t, pos: rope(t, pos, w.base)) if w.rope else (lambda t, pos: np.asarray(t, np.float64))
+    def rot(t, pos):
+        if not w.rope:
+            return np.asarray(t, np.float64)
+        r = rope(t, pos, w.base)
+        return round_bf16(r) if store_bf16 else r
     pos_ctx = np.arange(L)
     pos_q = L + np.arange(w.Lq)
     pos_d = L + w.Lq + np.arange(w.T)

@@ -101,22 +101,24 @@ def test_llama_workload(name):
     for bb in range(w.B):
         for kvh in kv_heads:
             log(f"{name}: oracle b={bb} kv head {kvh}")
-            K = so.rope(f64(x["k"][bb, kvh]), np.arange(w.L), w.base)
+            # rotated Q/K are stored in bf16 (the cache dtype) before attention
+            rot = lambda t, p: so.round_bf16(so.rope(t, p, w.base))
+            K = rot(f64(x["k"][bb, kvh]), np.arange(w.L))
             V = f64(x["v"][bb, kvh])
-            Kc = np.concatenate([K, so.rope(f64(x["kq"][bb, kvh]), pos_q, w.base),
-                                 so.rope(f64(x["kd"][bb, kvh]), pos_d, w.base)])
+            Kc = np.concatenate([K, rot(f64(x["kq"][bb, kvh]), pos_q),
+                                 rot(f64(x["kd"][bb, kvh]), pos_d)])
             Vc = np.concatenate([V, f64(x["vq"][bb, kvh]), f64(x["vd"][bb, kvh])])
             parts = so.partitions(w.L, w.b, w.cache_len)
             for h in range(kvh * g, (kvh + 1) * g):
-                qrows = so.rope(f64(x["q"][bb, h][pos]), pos, w.base)
+                qrows = rot(f64(x["q"][bb, h][pos]), pos)
                 ro, rl = so.phase1_rows(qrows, pos, K, V, w.b, w.a, scale)
                 go = host64(st.o1[bb, h].index_select(0, pos_t))
                 gl = host64(st.lse1[bb, h].index_select(0, pos_t))
                 e1 = check_out(go, ro, f"{name} phase1 O b{bb} h{h}")
                 e2 = check_lse(gl, rl, f"{name} phase1 LSE b{bb} h{h}")
                 # query rows and every decode step, against global attention
-                qq = so.rope(f64(x["qq"][bb, h]), pos_q, w.base)
-                qd = so.rope(f64(x["qd"][bb, h]), pos_d, w.base)
+                qq = rot(f64(x["qq"][bb, h]), pos_q)
+                qd = rot(f64(x["qd"][bb, h]), pos_d)
                 rows = np.concatenate([qq, qd])
                 rpos = np.concatenate([pos_q, pos_d])
                 o, l, _, _ = so.phase2(rows, rpos, Kc, Vc, parts, scale)

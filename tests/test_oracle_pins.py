@@ -366,3 +366,18 @@ def test_planted_mistakes(monkeypatch):
         m.setattr(so, "phase1", phase1_wrong_gqa)
         with pytest.raises(AssertionError):
             test_phase1_single_block_equals_dense_causal()
+
+
+def test_round_bf16_matches_torch_and_ties():
+    """bf16 rounding of the rotated tensors: equals torch's float32->bfloat16
+    cast (round to nearest even) on float32 inputs, and rounds float64
+    values directly (no double rounding through float32)."""
+    r = np.random.default_rng(5)
+    x = np.concatenate([r.standard_normal(50000) * 10.0 ** r.integers(-30, 30, 50000),
+                        [0.0, -0.0, 1.0, 1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 3e38]])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(so.round_bf16(x32.astype(np.float64)), ref)
+    assert so.round_bf16(np.array([1 + 2**-8 + 2**-40]))[0] == 1 + 2**-7
+    assert so.round_bf16(np.array([1 + 2**-8 - 2**-40]))[0] == 1.0
+    assert so.round_bf16(np.array([1 + 2**-8]))[0] == 1.0   # tie to even
