@@ -25,6 +25,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <cstdlib>
+
 namespace star {
 namespace {
 
@@ -452,8 +454,10 @@ hipError_t launch_cfg(FlashParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_flash(FlashParams& p, hipStream_t stream) {
-  if (p.D == 128) return launch_cfg<128, 4, 2>(p, stream);
-  return launch_cfg<64, 4, 2>(p, stream);
+  static const char* cfg = getenv("STAR_FLASH_CFG");
+  const bool wide = cfg != nullptr && cfg[0] == 'w';
+  if (p.D == 128) return wide ? launch_cfg<128, 4, 2>(p, stream) : launch_cfg<128, 8, 1>(p, stream);
+  return wide ? launch_cfg<64, 4, 2>(p, stream) : launch_cfg<64, 8, 1>(p, stream);
 }
 
 }  // namespace star

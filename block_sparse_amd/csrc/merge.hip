@@ -6,9 +6,6 @@
 // minor comment on Algorithm 2, and "Circularity Check").  Partials with
 // s_n = -inf (empty chunks, fully masked rows) get weight 0.
 //
-// One wave per row: lanes split the N statistics for the max and the sum
-// (wave reductions), then every lane accumulates D/64 output columns over
-// the N partials with coalesced loads of each partial's row.
 #include "common.h"
 #include "internal.h"
 
@@ -26,38 +23,81 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int MW = 8;  // waves per row
+
+// One workgroup per row.  Pass 1: all threads stride the N statistics for
+// the max and the sum of exp (block reductions through LDS).  Pass 2: wave w
+// takes partials w, w + MW, ...; each lane owns D/64 output columns; eight
+// partials' loads are issued before any is used, so a row costs a few
+// memory latencies whatever N is.  The MW waves' sums meet in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
-  constexpr int PER = D / 64;  // columns per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.R) return;
+__global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
+  constexpr int PER = D / 64;
+  constexpr int U = 8;
+  __shared__ float red[MW];
+  __shared__ float part[MW][D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const int N = p.N;
+  const float* ls = p.lsep + row;
+
   float m = -INFINITY;
-  for (int n = lane; n < N; n += 64) m = fmaxf(m, p.lsep[(int64_t)n * p.R + row]);
+  for (int n = tid; n < N; n += MW * 64) m = fmaxf(m, ls[(int64_t)n * p.R]);
   m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < MW; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  float lse = -INFINITY;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float lse = -INFINITY;
   if (m != -INFINITY) {
     float sum = 0.f;
-    for (int n = lane; n < N; n += 64) sum += __expf(p.lsep[(int64_t)n * p.R + row] - m);
+    for (int n = tid; n < N; n += MW * 64) sum += __expf(ls[(int64_t)n * p.R] - m);
     sum = wave_sum(sum);
+    if (lane == 0) red[wave] = sum;
+    __syncthreads();
+    sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) sum += red[w];
     lse = m + __logf(sum);
-    for (int n = 0; n < N; ++n) {
-      const float sn = p.lsep[(int64_t)n * p.R + row];
-      if (sn == -INFINITY) continue;
-      const float w = __expf(sn - lse);
-      const float* src = p.opart + ((int64_t)n * p.R + row) * D + lane * PER;
-      if constexpr (PER == 2) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(src);
-        acc[0] += w * v[0];
-        acc[1] += w * v[1];
-      } else {
-        acc[0] += w * src[0];
+    const float* ob = p.opart + row * D + lane * PER;
+    for (int n0 = wave; n0 < N; n0 += MW * U) {
+      float wt[U];
+      float v[U][PER];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * MW;
+        wt[u] = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[u][i] = 0.f;
+        if (n < N) {
+          const float sn = ls[(int64_t)n * p.R];
+          wt[u] = (sn == -INFINITY) ? 0.f : __expf(sn - lse);
+          const float* src = ob + (int64_t)n * p.R * D;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[u][i] = src[i];
+        }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += wt[u] * v[u][i];
     }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) part[wave][lane * PER + i] = acc[i];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) o += part[w][lane * PER + i];
+    acc[i] = o;
   }
   const int64_t s = row % p.S;
   const int64_t bh = row / p.S;
@@ -79,12 +119,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 hipError_t launch_merge(MergeParams& p, hipStream_t stream) {
   if (p.R <= 0) return hipSuccess;
-  const int64_t blocks = (p.R + 3) / 4;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.R > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)p.R), block(MW * 64);
   if (p.D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

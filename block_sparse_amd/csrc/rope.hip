@@ -70,25 +70,31 @@ __device__ __forceinline__ void store8<float>(float* p, const float* in) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{in[4], in[5], in[6], in[7]};
 }
 
-// grid-stride over (b, s, pair-chunk); loop over heads inside
+// grid-stride over (head group, b, s, pair-chunk); loop over the heads of
+// the group inside.  Long sequences use one group (sin/cos shared by all H
+// heads); a handful of rows (decode) spreads the heads over threads.
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(const RopeParams p) {
+__global__ __launch_bounds__(256) void rope_kernel(const RopeParams p, int hgroups) {
   const int nchunk = p.D / 16;  // chunks of 8 pairs per row
-  const int64_t total = (int64_t)p.B * p.S * nchunk;
+  const int64_t total = (int64_t)p.B * p.S * nchunk * hgroups;
   const int half = p.D / 2;
+  const int hper = (p.H + hgroups - 1) / hgroups;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int ch = (int)(idx % nchunk);
-    const int64_t bs = idx / nchunk;
-    const int64_t s = bs % p.S;
-    const int b = (int)(bs / p.S);
+    int64_t r = idx / nchunk;
+    const int64_t s = r % p.S;
+    r /= p.S;
+    const int b = (int)(r % p.B);
+    const int hg = (int)(r / p.B);
+    const int h0 = hg * hper, h1 = min(p.H, h0 + hper);
     const double pos = (double)(p.pos ? p.pos[s] : p.pos0 + s);
     float cs[8], sn[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) rope_angle(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
     const T* xb = reinterpret_cast<const T*>(p.x.data) + (int64_t)b * p.x.sB + s * p.x.sS;
     T* yb = reinterpret_cast<T*>(p.y) + (int64_t)b * p.ysB + s * p.ysS;
-    for (int h = 0; h < p.H; ++h) {
+    for (int h = h0; h < h1; ++h) {
       const T* xr = xb + (int64_t)h * p.x.sH;
       T* yr = yb + (int64_t)h * p.ysH;
       float x1[8], x2[8], y1[8], y2[8];
@@ -160,12 +166,14 @@ int grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_rope(RopeParams& p, hipStream_t stream) {
-  const int64_t total = (int64_t)p.B * p.S * (p.D / 16);
-  if (total <= 0 || p.H <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)p.B * p.S * (p.D / 16);
+  if (rows <= 0 || p.H <= 0) return hipSuccess;
+  const int hgroups = rows < 16384 ? p.H : 1;
+  const int64_t total = rows * hgroups;
   if (p.f32)
-    hipLaunchKernelGGL(rope_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(rope_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p, hgroups);
   else
-    hipLaunchKernelGGL(rope_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(rope_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, stream, p, hgroups);
   return hipGetLastError();
 }
 
