@@ -1,0 +1,346 @@
+// gfx950 flash kernel for bf16 Q/K/V with head dim 128: Phase 1 (anchor
+// block + own block, causal) and Phase-2 query-chunk partials.
+//
+// Same work decomposition and math as flash.hip (see flash_items.h for the
+// key ranges each row sees: Pith review of Star Attention, "What carries
+// the argument" and "Circularity Check"), re-planned around the costs the
+// hardware counters showed: the kernel is bound by VALU issue, not by MFMA.
+//  * K and V tiles go global -> LDS with global_load_lds_dwordx4: no staging
+//    registers, no ds_write, no VALU work.  A wave's load writes 1 KiB of
+//    LDS at consecutive addresses, so the chunk swizzle (see swz) is done by
+//    permuting the global source addresses instead.
+//  * V stays row-major in LDS; the V^T operand of the PV MFMA is read with
+//    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
+//    across each 16-lane group.
+//  * every LDS address is a per-lane constant plus an immediate: the tile
+//    loop is unrolled over the two buffers.
+//  * the softmax denominator is summed from the fp32 P before it is rounded
+//    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
+//    to 2^-9 relative).
+// One workgroup = 8 waves, one 32-row column block each; 64-key tiles,
+// double-buffered; two waves share a SIMD so one's softmax overlaps the
+// other's MFMAs.
+#include "common.h"
+#include "internal.h"
+#include "flash_items.h"
+
+#include <cstdlib>
+#include <type_traits>
+
+namespace star {
+namespace {
+
+constexpr int D = 128;
+constexpr int NW = 8;
+constexpr int KT = 64;
+constexpr int ROWB = D * 2;                 // bytes per K/V row
+constexpr int TILE = KT * ROWB;             // 16 KiB
+constexpr int BUF = 2 * TILE;               // K tile + V tile
+constexpr float kRescaleLog2 = 8.0f;
+constexpr int NBUF = 3;                     // LDS tile buffers
+
+// s_waitcnt vmcnt(4): all but this wave's last 4 vector-memory ops done
+// (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
+__device__ __forceinline__ void wait_vm_keep4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16-byte chunk c of LDS row r is stored at chunk c ^ swz(r & 15).  swz
+// takes the 4-row groups a transpose read touches (rows 4i..4i+3, two or
+// four adjacent chunks each) and the 16 rows a K read touches (one chunk
+// each) onto distinct banks, whether the LDS has 32 or 64 4-byte banks.
+__device__ __forceinline__ int swz(int r) {
+  const int k = r & 3;
+  const int g = (k << 1) | ((k ^ (k >> 1)) & 1);
+  return (2 * g) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
+#if __HIP_DEVICE_COMPILE__
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+#else
+  return s16x4{0, 0, 0, 0};
+#endif
+}
+
+__global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  Item it;
+  flash_get_item(p, xcd_remap(blockIdx.x, p.total_items), it);
+
+  const int64_t qlast = min(it.qr0 + p.m_pos, it.qr_end) - 1;
+  const int64_t pmax = qlast + p.pos_shift;
+  it.ra1 = max(min(min(it.ra1, pmax + 1), p.kv_rows), it.ra0);
+  it.rb1 = max(min(min(it.rb1, pmax + 1), p.kv_rows), it.rb0);
+
+  // this wave's column block: 32 consecutive positions of one query head
+  const int hh = wave % p.gw, pg = wave / p.gw;
+  const int hl = it.hg * p.gw + hh;
+  const int64_t r0 = it.qr0 + 32 * pg;
+  const bool cb_ok = (pg < p.npg) && (hl < p.g) && (r0 < it.qr_end);
+  const int head = it.kvh * p.g + (hl < p.g ? hl : 0);
+  const int64_t qrow = r0 + l32;
+  const bool row_ok = cb_ok && qrow < it.qr_end;
+  const int64_t wave_min = r0 + p.pos_shift;
+  const int64_t wave_max = cb_ok ? min(r0 + 31, it.qr_end - 1) + p.pos_shift : -1;
+  const int64_t qpos = qrow + p.pos_shift;
+
+  // Q^T operands (B of S^T = K Q^T): lane (query l32, half hf) holds
+  // d = 16dc + 8hf .. +7
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q.data) + (int64_t)it.b * p.q.sB +
+                       (int64_t)head * p.q.sH + (row_ok ? qrow : 0) * p.q.sS;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      u32x4 v = {0, 0, 0, 0};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qr + 16 * dc + 8 * hf);
+      qf[dc] = as_bf16x8(v);
+    }
+  }
+
+  // ---- per-lane constant LDS offsets
+  // K read for S^T: row 32kb + l32, logical chunk 2dc + hf
+  int kofs[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = l32 * ROWB + (((2 * dc + hf) ^ swz(l32)) << 4);
+  // V^T via transpose reads: 16-lane group G = lane >> 4 (h = G >> 1 selects
+  // keys 4h.., gsub = G & 1 selects d 16gsub..), lane j = lane & 15 points at
+  // row (8t + 4h + (j >> 2)) and columns 32db + 16gsub + 4(j & 3) .. +3
+  int vofs[2][D / 32];
+  {
+    const int j = lane & 15, G = lane >> 4, h = G >> 1, gsub = G & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int rr = 8 * t + 4 * h + (j >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c = 4 * db + 2 * gsub + ((j & 3) >> 1);
+        vofs[t][db] = rr * ROWB + ((c ^ swz(rr)) << 4) + 8 * (j & 1);
+      }
+    }
+  }
+
+  // ---- direct global -> LDS loads: wave w fills rows 8w .. 8w+7 of the
+  // K and V tiles, 4 rows (1 KiB) per instruction
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k.data) + (int64_t)it.b * p.k.sB +
+                        (int64_t)it.kvh * p.k.sH;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v.data) + (int64_t)it.b * p.v.sB +
+                        (int64_t)it.kvh * p.v.sH;
+  int lrow[2], lcol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lrow[i] = 8 * wave + 4 * i + (lane >> 4);
+    lcol[i] = 8 * ((lane & 15) ^ swz(lrow[i]));
+  }
+  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it)
+  auto load_tile = [&](int buf, int64_t kt) {
+    const bool full = kt + KT <= p.kv_rows;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int64_t key = kt + lrow[i];
+      if (!full) key = min(key, p.kv_rows - 1);
+      uint8_t* dk = smem + buf * BUF + (8 * wave + 4 * i) * ROWB;
+      __builtin_amdgcn_global_load_lds(kbase + key * p.k.sS + lcol[i], dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + key * p.v.sS + lcol[i], dk + TILE, 16, 0, 0);
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m2 = -INFINITY, lsum = 0.f;
+  const float c2 = p.scale_log2;
+
+  const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
+  const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
+  const int nsub = 2 * nt;                        // 32-key sub-tiles
+  auto tile_start = [&](int t) -> int64_t {
+    return t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0);
+  };
+
+  // Sub-tile j (32 keys) lives in LDS buffer (j / 2) % 3, rows 32 (j % 2) ..
+  // The loop below is unrolled over the 6 sub-tiles of one buffer cycle so
+  // that every LDS address is a per-lane constant plus an immediate.
+  auto qk = [&](auto boff) -> f32x16 {
+    constexpr int OFF = decltype(boff)::value;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+      s = mfma32(*reinterpret_cast<const bf16x8*>(smem + OFF + kofs[dc]), qf[dc], s);
+    return s;
+  };
+  // first key of sub-tile j, relative to the start of its key range, and
+  // the range it belongs to
+  auto sub_key = [&](int j) -> int64_t {
+    const int t = j >> 1;
+    return (t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0)) + 32 * (j & 1);
+  };
+  // keys of sub-tile j past the range end or after the row's position -> -inf
+  auto mask = [&](int j, f32x16& s) {
+    const int64_t ks = sub_key(j);
+    const int64_t rend = (j >> 1) < nt0 ? it.ra1 : it.rb1;
+    if (ks + 32 > rend || ks + 31 > wave_min) {
+      const int lim_end = (int)min(rend - ks, (int64_t)32);
+      const int lim_pos = (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= lim_end || key > lim_pos) s[r] = -INFINITY;
+      }
+    }
+  };
+
+  // prologue: tiles 0 and 1 in flight, wait for tile 0, first S
+  if (nt > 0) load_tile(0, tile_start(0));
+  if (nt > 1) load_tile(1, tile_start(1));
+  if (nt > 1) wait_vm_keep4(); else __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 s = {};
+  if (nsub > 0) {
+    s = qk(std::integral_constant<int, 0>{});
+    mask(0, s);
+  }
+
+  // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2)
+  auto step = [&](auto jjc, int j) {
+    constexpr int JJ = decltype(jjc)::value;
+    constexpr int CUR = (JJ >> 1) * BUF + (JJ & 1) * 32 * ROWB;          // this sub-tile
+    constexpr int JN = (JJ + 1) % 6;
+    constexpr int NXT = (JN >> 1) * BUF + (JN & 1) * 32 * ROWB;          // the next one
+    // row max of S_j (16 values in the lane + the partner half), lazy rescale
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mt2 = mt * c2;
+    const bool need = mt2 > m2 + kRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
+      if (need) m2 = mt2;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const bool more = j + 1 < nsub;
+    if constexpr ((JJ & 1) == 1) {
+      // the next sub-tile starts a new tile: make it resident, then put the
+      // tile after it in flight (its buffer was last read two tiles ago)
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int tn = (j >> 1) + 2;
+        if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tile_start(tn));
+      }
+    }
+    // P_j = exp2(S_j c - m): fp32 for the denominator, bf16 for PV; issued
+    // together with the next sub-tile's QK MFMAs (unconditional so they
+    // share a basic block; after the last sub-tile the result is unused)
+    const float msub = (m2 == -INFINITY) ? 0.f : m2;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, -msub));
+      lsum += pv;
+      pf[e >> 3][e & 7] = (__bf16)pv;
+    }
+    f32x16 sn = qk(std::integral_constant<int, NXT>{});
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const uint8_t* vb = smem + CUR + TILE + cc * 16 * ROWB;
+        const s16x4 a0 = tr_read(vb + vofs[0][db]);
+        const s16x4 a1 = tr_read(vb + vofs[1][db]);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = mfma32(a, pf[cc], oacc[db]);
+      }
+    if (more) mask(j + 1, sn);
+    s = sn;
+  };
+
+  for (int j = 0; j < nsub; j += 6) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 >= nsub) break;
+    step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 2 >= nsub) break;
+    step(std::integral_constant<int, 2>{}, j + 2);
+    if (j + 3 >= nsub) break;
+    step(std::integral_constant<int, 3>{}, j + 3);
+    if (j + 4 >= nsub) break;
+    step(std::integral_constant<int, 4>{}, j + 4);
+    if (j + 5 >= nsub) break;
+    step(std::integral_constant<int, 5>{}, j + 5);
+  }
+
+  // ---- epilogue
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  if (!row_ok) return;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lse = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
+  if (p.mode == 0) {
+    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)it.b * p.osB +
+                   (int64_t)head * p.osH + qrow * p.osS;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * hf;
+        u32x2 w = {pack_bf16(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv),
+                   pack_bf16(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+    if (p.lse != nullptr && hf == 0) p.lse[((int64_t)it.b * p.Hq + head) * p.L + qrow] = lse;
+  } else {
+    const int64_t row = (((int64_t)it.cs * p.B + it.b) * p.Hq + head) * p.q_rows + qrow;
+    float* orow = p.opart + row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * hf;
+        f32x4 w = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv,
+                   oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + d0) = w;
+      }
+    if (hf == 0) p.lse[row] = lse;
+  }
+}
+
+}  // namespace
+
+bool flash2_supported(const FlashParams& p) { return p.D == 128 && !p.in_f32; }
+
+hipError_t launch_flash2(FlashParams& p, hipStream_t stream) {
+  if (!flash_geometry(p, NW)) return hipErrorInvalidValue;
+  if (p.total_items == 0) return hipSuccess;
+  hipLaunchKernelGGL(flash2_kernel, dim3(p.total_items), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace star

@@ -46,6 +46,8 @@ struct FlashParams {
 };
 
 hipError_t launch_flash(FlashParams& p, hipStream_t stream);
+bool flash2_supported(const FlashParams& p);
+hipError_t launch_flash2(FlashParams& p, hipStream_t stream);
 
 // Split-KV decode partials (few query rows per KV head).
 struct DecodeParams {
