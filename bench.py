@@ -34,7 +34,7 @@ METRIC = "Phase1 context tokens/s + TFLOP/s; Phase2 decode GB/s (8B shapes, 128K
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "phase1_flash_llama8b-128k_pmc.txt")
-FLASH_SRC = os.path.join(ROOT, "block_sparse_amd", "csrc", "flash.hip")
+FLASH_SRC = os.path.join(ROOT, "block_sparse_amd", "csrc", "flash2.hip")
 
 
 def phase1_pairs(L: int, b: int, a: int) -> int:
@@ -123,8 +123,8 @@ def main():
                          "(reference kernel for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "
+              "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -204,7 +204,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
                      "traffic": pmc_traffic(),
-                     "kernel": "flash_kernel (Phase 1)"},
+                     "kernel": "flash2_kernel (Phase 1)"},
     }
     if not args.phase1_only and w.T > 0:
         dec_ms = np.mean([r["dec"][0].elapsed_time(r["dec"][1]) for r in recs])
