@@ -61,6 +61,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// global -> LDS DMA of 16 bytes per lane: lane i's bytes land at LDS address
+// lds + 16 i.  Issued from inline asm (inputs only: the address VGPRs are
+// read at issue, M0 is set in the same block) so that the compiler does not
+// treat it as a possibly-aliasing LDS store and wait for it before every
+// later LDS read; the kernel waits for it explicitly (vmcnt(0) + barrier)
+// before any wave reads the buffer.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
 __device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
 #if __HIP_DEVICE_COMPILE__
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -70,7 +87,12 @@ __device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
 }
 
 __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+  // three separate LDS objects, so that the compiler can tell a DMA into
+  // one buffer from reads of another and does not wait for it
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[BUF];
+  auto buf_ptr = [&](int b) -> uint8_t* { return b == 0 ? sm0 : (b == 1 ? sm1 : sm2); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,6 +132,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
       if (row_ok) v = *reinterpret_cast<const u32x4*>(qr + 16 * dc + 8 * hf);
       qf[dc] = as_bf16x8(v);
     }
+    // complete the Q loads before any (untracked) tile DMA is in flight, so
+    // the compiler never needs a vmcnt wait for them inside the key loop
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // ---- per-lane constant LDS offsets
@@ -153,9 +178,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     for (int i = 0; i < 2; ++i) {
       int64_t key = kt + lrow[i];
       if (!full) key = min(key, p.kv_rows - 1);
-      uint8_t* dk = smem + buf * BUF + (8 * wave + 4 * i) * ROWB;
-      __builtin_amdgcn_global_load_lds(kbase + key * p.k.sS + lcol[i], dk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + key * p.v.sS + lcol[i], dk + TILE, 16, 0, 0);
+      const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(buf_ptr(buf) + (8 * wave + 4 * i) * ROWB));
+      dma16(kbase + key * p.k.sS + lcol[i], dk);
+      dma16(vbase + key * p.v.sS + lcol[i], dk + TILE);
     }
   };
 
@@ -179,12 +204,13 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // that every LDS address is a per-lane constant plus an immediate.
   auto qk = [&](auto boff) -> f32x16 {
     constexpr int OFF = decltype(boff)::value;
+    const uint8_t* base = buf_ptr(OFF / BUF) + OFF % BUF;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
-      s = mfma32(*reinterpret_cast<const bf16x8*>(smem + OFF + kofs[dc]), qf[dc], s);
+      s = mfma32(*reinterpret_cast<const bf16x8*>(base + kofs[dc]), qf[dc], s);
     return s;
   };
   // first key of sub-tile j, relative to the start of its key range, and
@@ -273,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const uint8_t* vb = smem + CUR + TILE + cc * 16 * ROWB;
+        const uint8_t* vb = buf_ptr(CUR / BUF) + CUR % BUF + TILE + cc * 16 * ROWB;
         const s16x4 a0 = tr_read(vb + vofs[0][db]);
         const s16x4 a1 = tr_read(vb + vofs[1][db]);
         const bf16x8 a = __builtin_bit_cast(
