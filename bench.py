@@ -116,6 +116,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b-128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits-decode", type=int, default=None,
+                    help="chunks per KV partition for the decode partials")
+    ap.add_argument("--splits-query", type=int, default=None,
+                    help="chunks per KV partition for the query partials")
     ap.add_argument("--phase1-only", action="store_true",
                     help="time only RoPE + Phase 1 (for counter runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -137,7 +141,8 @@ def main():
     torch.cuda.set_device(0)
     x = inputs(w, as_bf16=True)
     dev = {n: torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).cuda() for n, t in x.items()}
-    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, w.Lq, w.T, rope=w.rope, base=w.base)
+    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, w.Lq, w.T, rope=w.rope, base=w.base,
+                           splits_query=args.splits_query, splits_decode=args.splits_decode)
     st.load_context(dev["v"])
     if args.copy_calib:
         n = args.copy_calib * (1 << 20) // 4

@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
-__all__ = ["rope_apply", "kv_append", "phase1_blocklocal", "phase2_partial",
+__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase2_partial",
            "lse_merge", "split_ranges", "StarError", "library"]
 
 
@@ -76,6 +76,16 @@ def kv_append(k_new, v_new, k_cache, v_cache, slot0: int, pos0: int,
     st = library().star_kv_append(*[ctypes.byref(x) for x in d], int(slot0), int(pos0),
                                   float(base), int(bool(rope)), _stream(k_new))
     _lib.check("star_kv_append", st)
+
+
+def decode_prepare(q_new, q_out, k_new, v_new, k_cache, v_cache, slot0: int, pos0: int,
+                   base: float = 500000.0, rope: bool = True):
+    """One launch: rotate ``q_new`` at positions ``pos0 + t`` into ``q_out``
+    and append ``k_new``/``v_new`` to the cache rows ``slot0 + t``."""
+    d = [_desc(t) for t in (q_new, q_out, k_new, v_new, k_cache, v_cache)]
+    st = library().star_decode_prepare(*[ctypes.byref(x) for x in d], int(slot0), int(pos0),
+                                       float(base), int(bool(rope)), _stream(q_new))
+    _lib.check("star_decode_prepare", st)
 
 
 def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,

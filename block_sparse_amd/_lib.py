@@ -23,7 +23,7 @@ STATUS = {
 }
 
 # every symbol include/star_attn.h declares
-EXPORTS = ("star_rope_apply", "star_kv_append", "star_phase1_blocklocal",
+EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase2_partial", "star_lse_merge", "star_status_string",
            "star_abi_version")
 
@@ -47,6 +47,7 @@ _i32, _i64, _f32, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.
 _SIGS = {
     "star_rope_apply": (ctypes.c_int, [_T, _T, _vp, _i64, _f64, _vp]),
     "star_kv_append": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
+    "star_decode_prepare": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp]),
     "star_phase2_partial": (ctypes.c_int, [_T, _T, _T, _P(_i64), _i32, _i32, _i64, _f32,
                                            _vp, _vp, _vp]),

@@ -108,9 +108,14 @@ int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int
   return hip_status(star::launch_rope(p, (hipStream_t)stream));
 }
 
-int star_kv_append(const star_tensor* k_new, const star_tensor* v_new, const star_tensor* k_cache,
+}  // extern "C"
+
+namespace {
+
+// Validation shared by star_kv_append and star_decode_prepare; fills p.
+int prepare_append(const star_tensor* k_new, const star_tensor* v_new, const star_tensor* k_cache,
                    const star_tensor* v_cache, int64_t slot0, int64_t pos0, double base,
-                   int32_t rope, void* stream) {
+                   int32_t rope, star::AppendParams& p) {
   int s;
   if ((s = check_tensor(k_new, false)) != STAR_OK) return s;
   if ((s = check_tensor(v_new, false)) != STAR_OK) return s;
@@ -125,8 +130,6 @@ int star_kv_append(const star_tensor* k_new, const star_tensor* v_new, const sta
   if (slot0 < 0 || pos0 < 0 || slot0 + T > k_cache->S) return STAR_ERR_SHAPE;
   if (rope && (!(base > 1.0) || !std::isfinite(base))) return STAR_ERR_SHAPE;
   if (B > 65535 || H > 65535) return STAR_ERR_UNSUPPORTED;
-  if (T == 0) return STAR_OK;
-  star::AppendParams p;
   std::memset(&p, 0, sizeof(p));
   p.kn = ref(k_new);
   p.vn = ref(v_new);
@@ -142,7 +145,45 @@ int star_kv_append(const star_tensor* k_new, const star_tensor* v_new, const sta
   p.pos0 = pos0;
   p.rope = rope != 0;
   if (rope) fill_inv_freq(p.inv_freq, D, base);
+  return STAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int star_kv_append(const star_tensor* k_new, const star_tensor* v_new, const star_tensor* k_cache,
+                   const star_tensor* v_cache, int64_t slot0, int64_t pos0, double base,
+                   int32_t rope, void* stream) {
+  star::AppendParams p;
+  const int s = prepare_append(k_new, v_new, k_cache, v_cache, slot0, pos0, base, rope, p);
+  if (s != STAR_OK) return s;
+  if (p.T == 0) return STAR_OK;
   return hip_status(star::launch_append(p, (hipStream_t)stream));
+}
+
+int star_decode_prepare(const star_tensor* q_new, const star_tensor* q_out,
+                        const star_tensor* k_new, const star_tensor* v_new,
+                        const star_tensor* k_cache, const star_tensor* v_cache, int64_t slot0,
+                        int64_t pos0, double base, int32_t rope, void* stream) {
+  star::PrepareParams p;
+  int s = prepare_append(k_new, v_new, k_cache, v_cache, slot0, pos0, base, rope, p.kv);
+  if (s != STAR_OK) return s;
+  if ((s = check_tensor(q_new, false)) != STAR_OK) return s;
+  if ((s = check_tensor(q_out, false)) != STAR_OK) return s;
+  if (q_new->B != k_new->B || q_new->S != k_new->S || q_new->D != k_new->D) return STAR_ERR_SHAPE;
+  if (q_out->B != q_new->B || q_out->H != q_new->H || q_out->S != q_new->S ||
+      q_out->D != q_new->D)
+    return STAR_ERR_SHAPE;
+  if (q_new->H < 1 || q_new->H > 65535) return STAR_ERR_UNSUPPORTED;
+  if (p.kv.T == 0) return STAR_OK;
+  p.qn = ref(q_new);
+  p.qo = q_out->data;
+  p.qosB = q_out->sB;
+  p.qosH = q_out->sH;
+  p.qosS = q_out->sS;
+  p.Hq = (int32_t)q_new->H;
+  return hip_status(star::launch_prepare(p, (hipStream_t)stream));
 }
 
 int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const star_tensor* v,

@@ -4,17 +4,19 @@
 // partition returns its local output and log-sum-exp (Pith review of Star
 // Attention, "Core claim" and "Circularity Check").  With one query token
 // the work is a stream over the whole KV cache, so this kernel is built to
-// keep HBM busy: every workgroup owns one chunk of one partition for one KV
-// head and all of its g query heads (GQA heads share each K/V byte read),
-// its four waves walk interleaved 32-key tiles of the chunk, and each wave
-// prefetches its next tile into registers (16-byte loads, 4 lanes per
-// 64-byte run of a key row) while it computes the current one.
+// keep HBM busy: one workgroup owns one long chunk of one partition for one
+// KV head and all of its g query heads (GQA heads share each K/V byte read),
+// its eight waves walk interleaved 32-key tiles of the chunk, and each wave
+// prefetches its next tile into registers (16-byte loads, four lanes per
+// 64-byte run of a key row) while it computes the current one.  Long chunks
+// keep the per-workgroup setup and the number of partials (and so the merge
+// that follows) small.
 //
 // Math on v_mfma_f32_16x16x32_bf16 with the g*Lq query rows padded to 16:
-// S^T = K Q^T (A = K straight from the loaded registers), the row
-// max/sum per lane column, then O^T += V^T P^T where V^T is read from a
-// per-wave LDS copy of the V tile (keys permuted to match the order the
-// S^T registers hold them) and P^T comes from the S^T registers.  The four
+// S^T = K Q^T (A = K straight from the loaded registers), the row max/sum
+// per lane column, then O^T += V^T P^T where V^T is read from a per-wave
+// LDS copy of the V tile with ds_read_b64_tr_b16 (keys in the order the
+// S^T registers hold them) and P^T comes from the S^T registers.  The
 // waves merge their (m, l, O) in LDS at the end.
 #include "common.h"
 #include "internal.h"
@@ -22,26 +24,47 @@
 namespace star {
 namespace {
 
-constexpr int NWD = 4;      // waves per workgroup
+constexpr int NWD = 8;      // waves per workgroup
 constexpr int KTD = 32;     // keys per wave tile
 constexpr float kRescaleLog2 = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
+#if __HIP_DEVICE_COMPILE__
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+#else
+  return s16x4{0, 0, 0, 0};
+#endif
+}
+
+// 16-byte chunk c of V-tile row r is stored at chunk c ^ swz(r & 15): the
+// 4-row x 2-chunk footprint of a transpose read and the 16-row footprint
+// of a row write land on distinct banks (32 or 64 banks of 4 bytes).
+__device__ __forceinline__ int swz(int r) {
+  const int k = r & 3;
+  const int g = (k << 1) | ((k ^ (k >> 1)) & 1);
+  return (2 * g) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+}
+
 template <int D>
-__device__ __forceinline__ int v_off(int key, int d) {
-  return key * (D * 2) + ((((d >> 3) ^ (key & 15)) & (D / 8 - 1)) << 4) + ((d & 7) << 1);
+__device__ __forceinline__ int v_chunk_off(int row, int chunk) {
+  return row * (D * 2) + (((chunk ^ swz(row)) & (D / 8 - 1)) << 4);
 }
 
 template <int D, typename T>
 __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) {
   constexpr int NDC = D / 32;   // k-steps of 32 along D
   constexpr int NDB = D / 16;   // 16-row blocks of O^T
+  constexpr int VT = KTD * D * 2;
   // per-wave V tiles during the key loop; reused for the final merge
-  static_assert(NWD * 16 * D * 4 <= NWD * KTD * D * 2, "merge buffer must fit");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NWD * KTD * D * 2];
+  static_assert(NWD * 16 * D * 4 <= NWD * VT, "merge buffer must fit");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NWD * VT];
   __shared__ float red_m[NWD][16];
   __shared__ float red_l[NWD][16];
   float (*red_o)[16][D] = reinterpret_cast<float (*)[16][D]>(smem);
@@ -70,8 +93,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const int qi = n / p.g;
   const int head = kvh * p.g + hh;
   const int64_t qpos = p.q_pos0 + qi;
-  // smallest row position (rows are ordered by query index)
-  const int64_t min_qpos = p.q_pos0;
+  const int64_t min_qpos = p.q_pos0;   // rows are ordered by query index
 
   // Q^T as the B operand: lane (row n, group kg) holds d = 32dc + 8kg + e.
   bf16x8 qf[NDC];
@@ -96,7 +118,28 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const float c2 = p.scale_log2;
 
   const int nt = (int)((c1 - c0 + KTD - 1) / KTD);
-  uint8_t* vs = smem + wave * (KTD * D * 2);
+  uint8_t* vs = smem + wave * VT;
+
+  // LDS offsets: row writes (row 16kb + n, chunk 4dc + kg) and transpose
+  // reads (16-lane group kg, lane j: row 16t + 4kg + (j >> 2), columns
+  // 16db + 4(j & 3) .. +3)
+  int wofs[2][NDC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) wofs[kb][dc] = v_chunk_off<D>(16 * kb + n, 4 * dc + kg);
+  int rofs[2][NDB];
+  {
+    const int j = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row = 16 * t + 4 * kg + (j >> 2);
+        const int col = 16 * db + 4 * (j & 3);
+        rofs[t][db] = v_chunk_off<D>(row, col >> 3) + ((col & 7) << 1);
+      }
+  }
 
   // register staging for one tile: [key block (16 keys)][d chunk]
   u32x4 kr[2][NDC], vr[2][NDC];
@@ -130,16 +173,14 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma16(as_bf16x8(kr[kb][dc]), qf[dc], s[kb]);
     }
-    // stage V (row-major, chunk-swizzled) in this wave's LDS region
+    // stage V (row-major, chunk-swizzled) in this wave's LDS region; the
+    // previous tile's transpose reads were issued before these writes, and
+    // LDS executes one wave's instructions in order
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const int key = 16 * kb + n;
-        const int d = 32 * dc + 8 * kg;
-        *reinterpret_cast<u32x4*>(vs + v_off<D>(key, d)) = vr[kb][dc];
-      }
+      for (int dc = 0; dc < NDC; ++dc) *reinterpret_cast<u32x4*>(vs + wofs[kb][dc]) = vr[kb][dc];
     asm volatile("" ::: "memory");
     // prefetch this wave's next tile while the current one is computed
     if (t + NWD < nt) load_tile(t + NWD);
@@ -181,19 +222,16 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
     // 4kg + e (e < 4) and 16 + 4kg + (e - 4), matching pt's order.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = 16 * db + n;
-      bf16x8 a;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = (e < 4) ? (4 * kg + e) : (16 + 4 * kg + e - 4);
-        a[e] = *reinterpret_cast<const __bf16*>(vs + v_off<D>(key, d));
-      }
+      const s16x4 a0 = tr_read(vs + rofs[0][db]);
+      const s16x4 a1 = tr_read(vs + rofs[1][db]);
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = mfma16(a, pt, oacc[db]);
     }
     asm volatile("" ::: "memory");
   }
 
-  // ---- merge the four waves' (m, l, O^T) and write the chunk partial
+  // ---- merge the waves' (m, l, O^T) and write the chunk partial
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   __syncthreads();  // every wave is done with its V tile

@@ -96,6 +96,17 @@ struct AppendParams {
 
 hipError_t launch_append(AppendParams& p, hipStream_t stream);
 
+// rope(q) + KV append of the same tokens in one launch
+struct PrepareParams {
+  AppendParams kv;
+  TensorRef qn;
+  void* qo;
+  int64_t qosB, qosH, qosS;
+  int32_t Hq;
+};
+
+hipError_t launch_prepare(PrepareParams& p, hipStream_t stream);
+
 struct MergeParams {
   const float* opart;
   const float* lsep;

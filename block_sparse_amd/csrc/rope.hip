@@ -158,6 +158,69 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   }
 }
 
+// rope(q) and the KV append of the same tokens: threads [0, nq) rotate
+// query rows, the rest handle K/V rows (one pair-chunk each)
+__global__ __launch_bounds__(256) void prepare_kernel(const PrepareParams pp) {
+  const AppendParams& p = pp.kv;
+  const int nchunk = p.D / 16;
+  const int half = p.D / 2;
+  const int64_t nq = (int64_t)p.B * pp.Hq * p.T * nchunk;
+  const int64_t nkv = (int64_t)p.B * p.H * p.T * nchunk;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nq + nkv;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const bool isq = idx < nq;
+    const int64_t li = isq ? idx : idx - nq;
+    const int ch = (int)(li % nchunk);
+    int64_t r = li / nchunk;
+    const int64_t t = r % p.T;
+    r /= p.T;
+    const int H = isq ? pp.Hq : p.H;
+    const int h = (int)(r % H);
+    const int b = (int)(r / H);
+    const __bf16* src;
+    __bf16* dst;
+    if (isq) {
+      src = reinterpret_cast<const __bf16*>(pp.qn.data) + (int64_t)b * pp.qn.sB +
+            (int64_t)h * pp.qn.sH + t * pp.qn.sS;
+      dst = reinterpret_cast<__bf16*>(pp.qo) + (int64_t)b * pp.qosB + (int64_t)h * pp.qosH +
+            t * pp.qosS;
+    } else {
+      src = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
+            (int64_t)h * p.kn.sH + t * p.kn.sS;
+      dst = reinterpret_cast<__bf16*>(p.kc) + (int64_t)b * p.kcsB + (int64_t)h * p.kcsH +
+            (p.slot0 + t) * p.kcsS;
+      const __bf16* vr = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
+                         (int64_t)h * p.vn.sH + t * p.vn.sS;
+      __bf16* vc = reinterpret_cast<__bf16*>(p.vc) + (int64_t)b * p.vcsB + (int64_t)h * p.vcsH +
+                   (p.slot0 + t) * p.vcsS;
+      *reinterpret_cast<u32x4*>(vc + 8 * ch) = *reinterpret_cast<const u32x4*>(vr + 8 * ch);
+      *reinterpret_cast<u32x4*>(vc + half + 8 * ch) =
+          *reinterpret_cast<const u32x4*>(vr + half + 8 * ch);
+    }
+    float x1[8], x2[8], y1[8], y2[8];
+    load8<__bf16>(src + 8 * ch, x1);
+    load8<__bf16>(src + half + 8 * ch, x2);
+    if (p.rope) {
+      const double pos = (double)(p.pos0 + t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float c, sn;
+        rope_angle(pos, p.inv_freq[8 * ch + i], c, sn);
+        y1[i] = x1[i] * c - x2[i] * sn;
+        y2[i] = x2[i] * c + x1[i] * sn;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y1[i] = x1[i];
+        y2[i] = x2[i];
+      }
+    }
+    store8<__bf16>(dst + 8 * ch, y1);
+    store8<__bf16>(dst + half + 8 * ch, y2);
+  }
+}
+
 int grid_for(int64_t total) {
   const int64_t blocks = (total + 255) / 256;
   return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
@@ -174,6 +237,13 @@ hipError_t launch_rope(RopeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(rope_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p, hgroups);
   else
     hipLaunchKernelGGL(rope_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, stream, p, hgroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare(PrepareParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.kv.B * (p.Hq + p.kv.H) * p.kv.T * (p.kv.D / 16);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prepare_kernel, dim3(grid_for(total)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ import math
 
 import torch
 
-from . import kv_append, lse_merge, phase1_blocklocal, phase2_partial, rope_apply
+from . import (decode_prepare, kv_append, lse_merge, phase1_blocklocal, phase2_partial,
+               rope_apply)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -69,7 +70,7 @@ class StarAttentionStep:
         self.P = -(-L // b)
         part_len = min(b, L)
         self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 512, 512)
-        self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 1536, 256)
+        self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 256, 512)
         nq = self.P * self.sq
         nd = self.P * self.sd
         self.op_q = torch.empty((nq, B, Hq, max(Lq, 1), D), dtype=torch.float32, device=dev)
@@ -116,11 +117,8 @@ class StarAttentionStep:
         """Generated token t (inputs are views [B, H, 1, D])."""
         pos = self.L + self.Lq + t
         qv = self.qd_r[:, :, t:t + 1]
-        if self.rope:
-            rope_apply(qd, pos0=pos, base=self.base, out=qv)
-        else:
-            qv.copy_(qd)
-        kv_append(kd, vd, self.kc, self.vc, slot0=pos, pos0=pos, base=self.base, rope=self.rope)
+        decode_prepare(qd, qv, kd, vd, self.kc, self.vc, slot0=pos, pos0=pos, base=self.base,
+                       rope=self.rope)
         offs = partition_offsets(self.L, self.b, pos + 1)
         phase2_partial(qv, self.kc, self.vc, offs, self.sd, q_pos0=pos, scale=self.scale,
                        o_part=self.op_d, lse_part=self.lp_d)

@@ -112,6 +112,25 @@ int star_kv_append(const star_tensor* k_new, const star_tensor* v_new,
                    void* stream);
 
 /*
+ * One generated token's (or a few query tokens') preparation in one launch:
+ * the new query rows are rotated at positions pos0 + t into q_out, and the
+ * new K/V rows are appended to the cache exactly as star_kv_append does
+ * (k rotated at pos0 + t into k_cache row slot0 + t, v copied).  Each
+ * generated token repeats Phase 2 with its own query and cached KV (Pith
+ * review of Star Attention, "What carries the argument" and "Core claim").
+ *
+ *   q_new, q_out      [B, Hq, T, D] bf16 (q_out may alias q_new exactly).
+ *   k_new, v_new      [B, Hkv, T, D] bf16.
+ *   k_cache, v_cache  [B, Hkv, S, D] bf16, slot0 + T <= S.
+ * With rope == 0 the rows are copied unrotated.
+ */
+int star_decode_prepare(const star_tensor* q_new, const star_tensor* q_out,
+                        const star_tensor* k_new, const star_tensor* v_new,
+                        const star_tensor* k_cache, const star_tensor* v_cache,
+                        int64_t slot0, int64_t pos0, double base, int32_t rope,
+                        void* stream);
+
+/*
  * Phase 1: anchor-block blockwise-local causal attention.
  * The context (length L = q->S) is cut into blocks [i*b, min((i+1)*b, L)).
  * Rows of the first block attend causally within it.  A row at position p

@@ -130,3 +130,11 @@ def test_merge_rope_append_validation(lib):
     assert a(8) == -2
     assert a(-1) == -2
     assert a(0, kk=T(B=1, H=2, S=11, D=128)) == -2
+    qn, qo = T(B=1, H=8, S=3, D=128), T(B=1, H=8, S=3, D=128)
+    dp = lambda q_in, q_o, slot=0: lib.star_decode_prepare(
+        ctypes.byref(q_in), ctypes.byref(q_o), ctypes.byref(kn), ctypes.byref(vn),
+        ctypes.byref(kc), ctypes.byref(vc), slot, 5, 5e5, 1, None)
+    assert dp(qn, T(B=1, H=8, S=4, D=128)) == -2
+    assert dp(T(B=1, H=8, S=2, D=128), T(B=1, H=8, S=2, D=128)) == -2
+    assert dp(qn, qo, slot=8) == -2
+    assert dp(T(B=1, H=8, S=3, D=128, data=0), qo) == -1

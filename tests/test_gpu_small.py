@@ -170,3 +170,27 @@ def test_kv_append_parity():
     assert (np.abs(got_k - ref_k) <= np.abs(ref_k) * 2.0**-8 + 1e-5).all()
     assert np.array_equal(host64(vc)[:, :, 30:35], f64(vn))
     assert (host64(kc)[:, :, :30] == 0).all() and (host64(kc)[:, :, 35:] == 0).all()
+
+
+@pytest.mark.parametrize("rope", [True, False])
+def test_decode_prepare_parity(rope):
+    """rope(q) + KV append in one launch equals the oracle rotation (bf16
+    rounding of the result) and leaves the rest of the cache untouched."""
+    B, Hq, Hkv, T, D, S = 2, 8, 2, 3, 128, 50
+    qn = rand_tensor(43, 6, B, Hq, T, D)
+    kn = rand_tensor(43, 7, B, Hkv, T, D)
+    vn = rand_tensor(43, 8, B, Hkv, T, D)
+    qo = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((B, Hkv, S, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    pos0 = 1048000
+    sa.decode_prepare(to_dev(qn), qo, to_dev(kn), to_dev(vn), kc, vc, slot0=40, pos0=pos0,
+                      base=500000.0, rope=rope)
+    torch.cuda.synchronize()
+    pos = pos0 + np.arange(T)
+    rq = so.rope(f64(qn), pos, 500000.0) if rope else f64(qn)
+    rk = so.rope(f64(kn), pos, 500000.0) if rope else f64(kn)
+    for got, ref in ((host64(qo), rq), (host64(kc)[:, :, 40:43], rk)):
+        assert (np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-5).all()
+    assert np.array_equal(host64(vc)[:, :, 40:43], f64(vn))
+    assert (host64(kc)[:, :, :40] == 0).all() and (host64(kc)[:, :, 43:] == 0).all()
