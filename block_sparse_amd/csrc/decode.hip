@@ -7,8 +7,8 @@
 // keep HBM busy: one workgroup owns one long chunk of one partition for one
 // KV head and all of its g query heads (GQA heads share each K/V byte read),
 // its eight waves walk interleaved 32-key tiles of the chunk, and each wave
-// prefetches its next tile into registers (16-byte loads, four lanes per
-// 64-byte run of a key row) while it computes the current one.  Long chunks
+// keeps its next two tiles in flight in registers (16-byte loads, four lanes
+// per 64-byte run of a key row) while it computes the current one.  Long chunks
 // keep the per-workgroup setup and the number of partials (and so the merge
 // that follows) small.
 //
@@ -20,6 +20,8 @@
 // waves merge their (m, l, O) in LDS at the end.
 #include "common.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace star {
 namespace {
@@ -141,9 +143,9 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       }
   }
 
-  // register staging for one tile: [key block (16 keys)][d chunk]
-  u32x4 kr[2][NDC], vr[2][NDC];
-  auto load_tile = [&](int t) {
+  // register staging, two tiles deep: [slot][key block (16 keys)][d chunk]
+  u32x4 kr[2][2][NDC], vr[2][2][NDC];
+  auto load_tile = [&](int slot, int t) {
     const int64_t kt = c0 + (int64_t)KTD * t;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -151,19 +153,20 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       const bool ok = key < c1;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        kr[kb][dc] = u32x4{0, 0, 0, 0};
-        vr[kb][dc] = u32x4{0, 0, 0, 0};
+        kr[slot][kb][dc] = u32x4{0, 0, 0, 0};
+        vr[slot][kb][dc] = u32x4{0, 0, 0, 0};
         if (ok) {
-          kr[kb][dc] = Load8<T>::load(kbase + key * p.k.sS + 32 * dc + 8 * kg);
-          vr[kb][dc] = Load8<T>::load(vbase + key * p.v.sS + 32 * dc + 8 * kg);
+          kr[slot][kb][dc] = Load8<T>::load(kbase + key * p.k.sS + 32 * dc + 8 * kg);
+          vr[slot][kb][dc] = Load8<T>::load(vbase + key * p.v.sS + 32 * dc + 8 * kg);
         }
       }
     }
   };
 
-  int t = wave;
-  if (t < nt) load_tile(t);
-  for (; t < nt; t += NWD) {
+  // one tile held in staging slot SL; the slot is refilled with the tile
+  // two steps ahead right after its registers are consumed
+  auto process = [&](auto slc, int t) {
+    constexpr int SL = decltype(slc)::value;
     const int64_t kt = c0 + (int64_t)KTD * t;
     // S^T = K Q^T for two 16-key blocks
     f32x4 s[2];
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma16(as_bf16x8(kr[kb][dc]), qf[dc], s[kb]);
+      for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma16(as_bf16x8(kr[SL][kb][dc]), qf[dc], s[kb]);
     }
     // stage V (row-major, chunk-swizzled) in this wave's LDS region; the
     // previous tile's transpose reads were issued before these writes, and
@@ -180,10 +183,10 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) *reinterpret_cast<u32x4*>(vs + wofs[kb][dc]) = vr[kb][dc];
+      for (int dc = 0; dc < NDC; ++dc)
+        *reinterpret_cast<u32x4*>(vs + wofs[kb][dc]) = vr[SL][kb][dc];
     asm volatile("" ::: "memory");
-    // prefetch this wave's next tile while the current one is computed
-    if (t + NWD < nt) load_tile(t + NWD);
+    if (t + 2 * NWD < nt) load_tile(SL, t + 2 * NWD);
 
     // mask: keys past the chunk end or after the row's position
     if (kt + KTD > c1 || kt + KTD - 1 > min_qpos) {
@@ -229,6 +232,15 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       oacc[db] = mfma16(a, pt, oacc[db]);
     }
     asm volatile("" ::: "memory");
+  };
+
+  // this wave's tiles: wave, wave + NWD, ...; two in flight at any time
+  if (wave < nt) load_tile(0, wave);
+  if (wave + NWD < nt) load_tile(1, wave + NWD);
+  for (int t = wave; t < nt; t += 2 * NWD) {
+    process(std::integral_constant<int, 0>{}, t);
+    if (t + NWD >= nt) break;
+    process(std::integral_constant<int, 1>{}, t + NWD);
   }
 
   // ---- merge the waves' (m, l, O^T) and write the chunk partial
