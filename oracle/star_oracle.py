@@ -37,7 +37,12 @@ Readings where the pages leave a step open (all listed in the design notes):
   * the query host is the last partition: it also holds the query and decode
     tokens' KV, and a token attends to itself;
   * RoPE is rotate-half with theta_j = base^(-2j/D), angles in exact (fp64)
-    arithmetic, no frequency scaling.
+    arithmetic, no frequency scaling;
+  * a prefix (anchor variant or Pulsar sink + summaries) precedes its block:
+    every block row sees every prefix key;
+  * Pulsar: host 0 is plain causal; block 0's chunks that overlap the sink
+    are not summary candidates; equal Max-IDF scores go to the earlier chunk;
+    the last chunk of a block may be shorter than m.
 """
 from __future__ import annotations
 
@@ -338,3 +343,172 @@ def star_attention(w, x: dict, store_bf16: bool = True):
                 OD[bb, h, t], LD[bb, h, t] = o[0], l[0]
     res.update(O2=O2, LSE2=L2, P2o=P2o, P2l=P2l, OD=OD, LSED=LD)
     return res
+
+
+# ----------------------------------------------------------------------------
+# Phase 1 with an explicit per-block prefix (anchor variants and Pulsar)
+# ----------------------------------------------------------------------------
+def phase1_prefix_keys(n_prefix: int, n_block: int, rows=None):
+    """Mask of one augmented block [prefix ; own block]: every row sees all
+    ``n_prefix`` prefix keys (they precede the block) and its own block's
+    keys up to itself.  Returns mask[len(rows), n_prefix + n_block]."""
+    r = np.arange(n_block) if rows is None else np.asarray(rows)
+    causal = np.arange(n_block)[None, :] <= r[:, None]
+    return np.concatenate([np.ones((r.size, n_prefix), dtype=bool), causal], axis=1)
+
+
+def phase1_prefix(Q, K, V, PK, PV, starts, lens, b: int, scale: float):
+    """Phase 1 where block i's prefix is rows [starts[i], starts[i] + lens[i])
+    of PK/PV instead of the fixed anchor.
+
+    This is the common form of the anchor variants the Star Attention pages
+    ablate ([SA-atlas] "Measured effects reported in the paper": no anchor,
+    anchor with other position ids, anchor with other content) and of the
+    Pulsar prefix ([Pulsar] "What carries the argument": host i encodes
+    [sink || summaries of blocks 0..i-1 || B_i] and then drops the prefix
+    KV).  Q [B, Hq, L, D]; K/V [B, Hkv, L, D]; PK/PV [B, Hkv, R, D].
+    Returns O [B, Hq, L, D] and LSE [B, Hq, L].
+    """
+    B, Hq, L, D = Q.shape
+    g = Hq // K.shape[1]
+    O = np.zeros((B, Hq, L, D))
+    LSE = np.full((B, Hq, L), NEG_INF)
+    for i, (s, e) in enumerate(blocks(L, b)):
+        p0, p1 = int(starts[i]), int(starts[i]) + int(lens[i])
+        mask = phase1_prefix_keys(p1 - p0, e - s)
+        for bb in range(B):
+            for h in range(Hq):
+                kv = h // g
+                keys = np.concatenate([PK[bb, kv, p0:p1], K[bb, kv, s:e]])
+                vals = np.concatenate([PV[bb, kv, p0:p1], V[bb, kv, s:e]])
+                o, l = attend(Q[bb, h, s:e], keys, vals, mask, scale)
+                O[bb, h, s:e], LSE[bb, h, s:e] = o, l
+    return O, LSE
+
+
+def phase1_prefix_rows(q_rows, pos, K, V, PK, PV, starts, lens, b: int, scale: float):
+    """:func:`phase1_prefix` for selected rows of one (batch, query head):
+    ``q_rows[n, D]`` at context positions ``pos[n]``; K/V [L, D] and PK/PV
+    [R, D] are that head's KV head."""
+    L = K.shape[0]
+    pos = np.asarray(pos)
+    o = np.zeros((pos.size, V.shape[1]))
+    lse = np.full(pos.size, NEG_INF)
+    for i, (s, e) in enumerate(blocks(L, b)):
+        sel = np.nonzero((pos >= s) & (pos < e))[0]
+        if sel.size == 0:
+            continue
+        p0, p1 = int(starts[i]), int(starts[i]) + int(lens[i])
+        mask = phase1_prefix_keys(p1 - p0, e - s, rows=pos[sel] - s)
+        keys = np.concatenate([PK[p0:p1], K[s:e]])
+        vals = np.concatenate([PV[p0:p1], V[s:e]])
+        oo, ll = attend(q_rows[sel], keys, vals, mask, scale)
+        o[sel], lse[sel] = oo, ll
+    return o, lse
+
+
+def anchor_prefix_table(L: int, b: int, a: int):
+    """The Star anchor as a prefix table over the context K/V themselves:
+    block 0 has none, block i >= 1 has rows [0, a) ([SA-pith] "What carries
+    the argument")."""
+    n = len(blocks(L, b))
+    starts = np.zeros(n, dtype=np.int64)
+    lens = np.array([0] + [min(a, L)] * (n - 1), dtype=np.int64)
+    return starts, lens
+
+
+def remapped_anchor(K_pre, pos_per_block, base: float, store_bf16: bool = True):
+    """Anchor keys re-rotated at other position ids, one copy per block.
+
+    The position-id ablation ([SA-atlas] "Measured effects reported in the
+    paper"; [SA-pith] "Core claim": the content of the anchor matters, its
+    position ids much less) keeps the anchor's content (the first ``a``
+    context tokens, un-rotated keys ``K_pre[..., :a, :]``) and rotates it at
+    ``pos_per_block[i]`` (``a`` positions) for block i.  Row block i of the
+    result (rows [i*a, (i+1)*a)) is that block's anchor; block 0's slot is
+    unused.  Values need no rotation: the anchor V is block 1's V.
+    """
+    K_pre = np.asarray(K_pre, dtype=np.float64)
+    out = []
+    for pos in pos_per_block:
+        pos = np.asarray(pos)
+        r = rope(K_pre[..., :pos.size, :], pos, base)
+        out.append(round_bf16(r) if store_bf16 else r)
+    return np.concatenate(out, axis=-2)
+
+
+# ----------------------------------------------------------------------------
+# Pulsar: attention sink + Max-IDF chunk summaries of the earlier blocks
+# ----------------------------------------------------------------------------
+def chunks_of_block(s: int, e: int, m: int):
+    """Chunks of m consecutive tokens of block [s, e) ([Pulsar] "What
+    carries the argument": chunks of 32 tokens); the last one is shorter
+    when m does not divide the block length."""
+    return [(c, min(c + m, e)) for c in range(s, e, m)]
+
+
+def document_frequency(tokens, L: int, b: int) -> dict:
+    """df(t) = number of blocks that contain token t ([Pulsar] "What carries
+    the argument")."""
+    df = {}
+    for s, e in blocks(L, b):
+        for t in set(int(x) for x in tokens[s:e]):
+            df[t] = df.get(t, 0) + 1
+    return df
+
+
+def maxidf_score(chunk_tokens, df: dict, n: int) -> float:
+    """score(C) = max over the chunk's tokens of IDF(t) = log(n / max(df(t), 1))
+    ([Pulsar] "What carries the argument")."""
+    return max(math.log(n / max(df.get(int(t), 0), 1)) for t in chunk_tokens)
+
+
+def maxidf_summaries(tokens, L: int, b: int, m: int, sink: int, k: int):
+    """Summary Sigma_i of every block: its k best chunks by Max-IDF score,
+    listed in positional order ([Pulsar] "What carries the argument", "Core
+    claim").  Readings: equal scores go to the earlier chunk; block 0's
+    chunks that overlap the sink are not candidates (those tokens are already
+    in every prefix); a block with fewer candidates than k keeps them all.
+    Returns a list of token-index arrays, one per block.
+    """
+    bl = blocks(L, b)
+    n = len(bl)
+    df = document_frequency(tokens, L, b)
+    out = []
+    for i, (s, e) in enumerate(bl):
+        cands = [(c0, c1) for (c0, c1) in chunks_of_block(s, e, m)
+                 if not (i == 0 and c0 < sink)]
+        scored = [(-maxidf_score(tokens[c0:c1], df, n), c0, c1) for (c0, c1) in cands]
+        best = sorted(scored)[:k]                      # highest score, then earliest
+        best = sorted(best, key=lambda t: t[1])        # positional order
+        rows = [np.arange(c0, c1) for (_, c0, c1) in best]
+        out.append(np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64))
+    return out
+
+
+def pulsar_prefix(tokens, L: int, b: int, m: int = 32, sink: int = 64, k: int = 16):
+    """Host i's prefix [sink || Sigma_0 || ... || Sigma_{i-1}] ([Pulsar] "What
+    carries the argument") as one list of context rows plus a per-block
+    table into it: block i's prefix is rows[starts[i] : starts[i] + lens[i]].
+    Reading: host 0 is plain causal over its own block (its sink is its own
+    first tokens), as Star's first block carries no anchor.
+    Returns (rows[R], starts[n], lens[n]).
+    """
+    sums = maxidf_summaries(tokens, L, b, m, sink, k)
+    n = len(sums)
+    sink_rows = np.arange(min(sink, L, b))
+    rows = [sink_rows] + sums[:-1]
+    rows = np.concatenate(rows).astype(np.int64)
+    starts = np.zeros(n, dtype=np.int64)
+    lens = np.zeros(n, dtype=np.int64)
+    for i in range(1, n):
+        lens[i] = sink_rows.size + sum(x.size for x in sums[:i])
+    return rows, starts, lens
+
+
+def pulsar_host_length(L: int, b: int, sink: int, s: int, i: int) -> int:
+    """Tokens host i encodes in Phase 1 when every summary has s tokens:
+    b + sink + i*s (host 0: b) ([Pulsar] "Referee Report", major comment 1,
+    and Eq. 4 as restated there)."""
+    n_i = min(b, L - i * b)
+    return n_i if i == 0 else n_i + sink + i * s

@@ -52,3 +52,26 @@ def test_workload_table():
         "tiny", "llama8b-16k", "llama8b-128k", "llama70b-64k", "llama8b-1m"]
     w = L8B_128K
     assert (w.n_blocks, w.g, w.a, w.cache_len) == (8, 4, 16384, 131072 + 64 + 128)
+
+
+def test_token_ids_seeded_and_zipf_shaped():
+    from workloads import VOCAB, token_ids
+    a, b = token_ids(2, 2, 4096), token_ids(2, 2, 4096)
+    assert a.dtype == np.int32 and a.shape == (2, 4096)
+    assert np.array_equal(a, b) and not np.array_equal(a[0], a[1])
+    assert a.min() >= 0 and a.max() < VOCAB
+    # a heavy head and a long tail: the most frequent id is far above the
+    # median count, and many ids occur once
+    _, counts = np.unique(a[0], return_counts=True)
+    assert counts.max() > 20 * np.median(counts) and (counts == 1).sum() > 500
+
+
+def test_anchor_positions_precede_their_block():
+    from workloads import anchor_positions
+    L, b, a = 1000, 200, 150
+    pos = anchor_positions(3, L, b, a)
+    assert len(pos) == 5 and np.array_equal(pos[0], np.arange(a))
+    for i in range(1, 5):
+        p = pos[i]
+        assert p.size == a and np.all(np.diff(p) > 0) and p.min() >= 0 and p.max() < i * b
+    assert all(np.array_equal(x, y) for x, y in zip(pos, anchor_positions(3, L, b, a)))

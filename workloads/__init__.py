@@ -40,6 +40,11 @@ CHUNK_ROWS = 4096
 T_Q, T_K, T_V = 0, 1, 2            # context Q/K/V (pre-RoPE)
 T_QQ, T_KQ, T_VQ = 3, 4, 5         # query tokens (Phase 2)
 T_QD, T_KD, T_VD = 6, 7, 8         # decode tokens (Phase 2, one per step)
+T_TOK = 9                          # context token ids (Pulsar chunk scoring)
+T_APOS = 10                        # anchor position ids (position-id ablation)
+
+VOCAB = 128256                     # Llama-3 vocabulary size
+ZIPF_S = 1.1                       # exponent of the token-rank distribution
 
 
 @dataclasses.dataclass(frozen=True)
@@ -194,3 +199,53 @@ def as_f64(t: np.ndarray) -> np.ndarray:
     if t.dtype == np.uint16:
         return bf16_bits_to_f32(t).astype(np.float64)
     return t.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# inputs of the Phase-1 prefix variants
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PulsarParams:
+    """Pulsar's free parameters (Pulsar review page, "Assumptions & free
+    parameters"): chunk of m tokens, a sink of ``sink`` tokens, and k chunks
+    per block, i.e. a summary budget of 12.5% of the block (16 chunks of 32
+    for a 4096-token block, scaled with the block)."""
+    m: int = 32
+    sink: int = 64
+    k: int = 16
+
+
+def pulsar_params(w: Workload) -> PulsarParams:
+    return PulsarParams(m=32, sink=64, k=max(1, w.b // 256))
+
+
+def token_ids(seed: int, B: int, L: int) -> np.ndarray:
+    """Synthetic context token ids [B, L] (int32).  Token ranks follow a
+    Zipf law p(r) ~ r^-ZIPF_S over the VOCAB ranks (a few frequent tokens,
+    a long tail of rare ones, as in text); ranks map to ids through a seeded
+    permutation.  The pages score chunks by the rarity of their tokens, so
+    only the frequency structure matters, not which ids carry it."""
+    ranks = np.arange(1, VOCAB + 1, dtype=np.float64)
+    cdf = np.cumsum(ranks ** -ZIPF_S)
+    cdf /= cdf[-1]
+    out = np.empty((B, L), dtype=np.int32)
+    for b in range(B):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, T_TOK, b])))
+        perm = rng.permutation(VOCAB)
+        r = np.searchsorted(cdf, rng.random(L), side="right")
+        out[b] = perm[np.minimum(r, VOCAB - 1)]
+    return out
+
+
+def anchor_positions(seed: int, L: int, b: int, a: int) -> list:
+    """Position ids for the anchor of every block in the position-id
+    ablation: for block i >= 1, ``a`` distinct positions drawn uniformly
+    from [0, i*b) (positions before the block), sorted.  Block 0 (no
+    anchor) gets its original positions 0..a-1 as a placeholder."""
+    n = -(-L // b)
+    a = min(a, L)
+    out = [np.arange(a, dtype=np.int64)]
+    for i in range(1, n):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, T_APOS, i])))
+        out.append(np.sort(rng.choice(i * b, size=a, replace=False)).astype(np.int64))
+    return out
