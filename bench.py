@@ -110,18 +110,22 @@ def cpu_baseline(w, x):
 
 
 def decode_cold(st, dev, w, ev, samples=16):
-    """Decode steps timed one at a time after a 1 GiB device write between
-    them, which evicts the L2 caches and the 256 MiB Infinity Cache, so every
-    K/V byte comes from HBM.  Re-runs decode steps spread over 0..T-1 after
-    the timed pass (the cache rows they append hold the same values)."""
+    """Decode steps timed one at a time, each after a 1 GiB device read that
+    evicts the L2 caches and the 256 MiB Infinity Cache, so every K/V byte
+    comes from HBM.  The flush reads rather than writes: a written flush
+    leaves dirty lines whose write-back then competes with the timed reads
+    (it halves a plain streaming read's rate on this chip).  Re-runs decode
+    steps spread over 0..T-1 after the timed pass (the cache rows they
+    append hold the same values)."""
     import numpy as np
     import torch
 
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     ts = sorted(set(np.linspace(0, w.T - 1, min(samples, w.T)).astype(int).tolist()))
     recs = []
     for i, t in enumerate(ts):
-        flush.fill_(float(i))
+        torch.sum(flush, dtype=torch.float32, out=sink)
         e0, e1 = ev(), ev()
         e0.record()
         st.decode(t, dev["qd"][:, :, t:t + 1], dev["kd"][:, :, t:t + 1],
@@ -136,7 +140,7 @@ def decode_cold(st, dev, w, ev, samples=16):
     del flush
     return {"us_per_step": us, "gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBS,
             "steps_sampled": len(ts),
-            "note": "each step after a 1 GiB write that flushes L2 and Infinity Cache"}
+            "note": "each step after a 1 GiB read that flushes L2 and Infinity Cache"}
 
 
 def main():

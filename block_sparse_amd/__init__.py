@@ -6,7 +6,9 @@ pick the current HIP stream and call the library.  Every step of the
 computation runs in the library's HIP kernels.  PyTorch provides device
 memory and streams only; tensors must live on a ROCm device.
 
-Phase 1 -- anchor-block blockwise-local causal attention (context encoding).
+Phase 1 -- anchor-block blockwise-local causal attention (context encoding),
+           or the same with any per-block prefix (anchor ablations, Pulsar's
+           sink + Max-IDF summaries).
 Phase 2 -- per-partition partials + exact LSE merge (query and decode).
 """
 from __future__ import annotations
@@ -19,8 +21,9 @@ import torch
 from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
-__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase2_partial",
-           "lse_merge", "split_ranges", "StarError", "library"]
+__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_prefix",
+           "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "split_ranges",
+           "StarError", "library"]
 
 
 def library():
@@ -111,6 +114,80 @@ def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,
         float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
     _lib.check("star_phase1_blocklocal", st)
     return out, lse
+
+
+def phase1_prefix(q, k, v, pk, pv, prefix_start, prefix_len, block_b: int,
+                  scale: float | None = None, out=None, lse=None, want_lse: bool = False):
+    """Phase 1 where block i attends to all of ``pk/pv`` rows
+    ``[prefix_start[i], prefix_start[i] + prefix_len[i])`` and then causally
+    within itself.  ``prefix_start``/``prefix_len`` are host sequences of
+    ceil(L / block_b) ints.  Returns ``(o, lse)``."""
+    B, Hq, L, D = q.shape
+    n = -(-L // block_b)
+    if len(prefix_start) != n or len(prefix_len) != n:
+        raise ValueError(f"prefix table needs {n} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq * L):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, L] tensor")
+    st_arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in prefix_start])
+    ln_arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in prefix_len])
+    d = [_desc(t) for t in (q, k, v, pk, pv)]
+    do = _desc(out)
+    st = library().star_phase1_prefix(*[ctypes.byref(x) for x in d], st_arr, ln_arr, int(n),
+                                      int(block_b), float(scale), ctypes.byref(do), _ptr(lse),
+                                      _stream(q))
+    _lib.check("star_phase1_prefix", st)
+    return out, lse
+
+
+def gather_rows(src, rows, out=None):
+    """``out[b, h, r] = src[b, h, rows[r]]`` (``rows`` device int64)."""
+    if rows.dtype != torch.int64 or not rows.is_contiguous() or rows.dim() != 1:
+        raise ValueError("rows must be a contiguous 1-D int64 tensor")
+    B, H, _, D = src.shape
+    if out is None:
+        out = torch.empty((B, H, rows.numel(), D), dtype=src.dtype, device=src.device)
+    if out.shape[2] != rows.numel():
+        raise ValueError("out must have one row per index")
+    a, b = _desc(src), _desc(out)
+    st = library().star_gather_rows(ctypes.byref(a), _ptr(rows), ctypes.byref(b), _stream(src))
+    _lib.check("star_gather_rows", st)
+    return out
+
+
+def pulsar_prefix(tokens, L: int, block_b: int, chunk_m: int = 32, sink: int = 64,
+                  k: int = 16):
+    """Pulsar's prefix rows and per-block table from host token ids (the
+    library's host-side Max-IDF selection).  Returns numpy int64
+    ``(rows[R], prefix_start[n], prefix_len[n])``."""
+    import numpy as np
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    if tok.shape != (L,):
+        raise ValueError("tokens must be a 1-D array of L ids")
+    n = -(-L // block_b)
+    st = np.zeros(max(n, 1), dtype=np.int64)
+    ln = np.zeros(max(n, 1), dtype=np.int64)
+    nrows = ctypes.c_int64(0)
+    P64 = ctypes.POINTER(ctypes.c_int64)
+    tptr = tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    lib = library()
+    args = (tptr, int(L), int(block_b), int(chunk_m), int(sink), int(k))
+    r = lib.star_pulsar_prefix(*args, None, 0, ctypes.byref(nrows), st.ctypes.data_as(P64),
+                               ln.ctypes.data_as(P64), int(n))
+    if r not in (0, _lib.STATUS_CODE["STAR_ERR_SHAPE"]):
+        _lib.check("star_pulsar_prefix", r)
+    rows = np.zeros(max(nrows.value, 1), dtype=np.int64)
+    r = lib.star_pulsar_prefix(*args, rows.ctypes.data_as(P64), int(rows.size),
+                               ctypes.byref(nrows), st.ctypes.data_as(P64),
+                               ln.ctypes.data_as(P64), int(n))
+    _lib.check("star_pulsar_prefix", r)
+    return rows[:nrows.value], st[:n], ln[:n]
 
 
 def split_ranges(part_offsets, splits: int):

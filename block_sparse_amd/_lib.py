@@ -21,9 +21,11 @@ STATUS = {
     0: "STAR_OK", -1: "STAR_ERR_NULL", -2: "STAR_ERR_SHAPE", -3: "STAR_ERR_DTYPE",
     -4: "STAR_ERR_ALIGN", -5: "STAR_ERR_UNSUPPORTED", -6: "STAR_ERR_HIP",
 }
+STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # every symbol include/star_attn.h declares
 EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
+           "star_phase1_prefix", "star_gather_rows", "star_pulsar_prefix",
            "star_phase2_partial", "star_lse_merge", "star_status_string",
            "star_abi_version")
 
@@ -49,6 +51,11 @@ _SIGS = {
     "star_kv_append": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_decode_prepare": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp]),
+    "star_phase1_prefix": (ctypes.c_int, [_T, _T, _T, _T, _T, _P(_i64), _P(_i64), _i32, _i64,
+                                          _f32, _T, _vp, _vp]),
+    "star_gather_rows": (ctypes.c_int, [_T, _vp, _T, _vp]),
+    "star_pulsar_prefix": (ctypes.c_int, [_P(_i32), _i64, _i64, _i32, _i32, _i32, _P(_i64), _i64,
+                                          _P(_i64), _P(_i64), _P(_i64), _i32]),
     "star_phase2_partial": (ctypes.c_int, [_T, _T, _T, _P(_i64), _i32, _i32, _i64, _f32,
                                            _vp, _vp, _vp]),
     "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _T, _vp, _vp]),

@@ -58,6 +58,50 @@ int check_qkv(const star_tensor* q, const star_tensor* k, const star_tensor* v) 
   return STAR_OK;
 }
 
+// Validation shared by the two Phase-1 entry points.
+int check_phase1(const star_tensor* q, const star_tensor* k, const star_tensor* v,
+                 int64_t block_b, float scale, const star_tensor* o, const float* lse) {
+  int s;
+  if ((s = check_qkv(q, k, v)) != STAR_OK) return s;
+  if ((s = check_tensor(o, false)) != STAR_OK) return s;
+  if (k->S != q->S) return STAR_ERR_SHAPE;
+  if (o->B != q->B || o->H != q->H || o->S != q->S || o->D != q->D) return STAR_ERR_SHAPE;
+  if (block_b < 1) return STAR_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  return STAR_OK;
+}
+
+// Phase-1 launch parameters common to both entry points (key range A is
+// filled by the caller).
+void phase1_params(star::FlashParams& p, const star_tensor* q, const star_tensor* k,
+                   const star_tensor* v, int64_t block_b, float scale, const star_tensor* o,
+                   float* lse) {
+  std::memset(&p, 0, sizeof(p));
+  p.q = ref(q);
+  p.k = ref(k);
+  p.v = ref(v);
+  p.B = (int32_t)q->B;
+  p.Hq = (int32_t)q->H;
+  p.Hkv = (int32_t)k->H;
+  p.g = p.Hq / p.Hkv;
+  p.D = (int32_t)q->D;
+  p.in_f32 = q->dtype == STAR_F32;
+  p.q_rows = q->S;
+  p.kv_rows = k->S;
+  p.pos_shift = 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mode = 0;
+  p.L = q->S;
+  p.b = block_b < q->S ? block_b : q->S;
+  p.o = o->data;
+  p.osB = o->sB;
+  p.osH = o->sH;
+  p.osS = o->sS;
+  p.lse = lse;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,7 +119,7 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 100; }
+int star_abi_version(void) { return 200; }
 
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
                     int64_t pos0, double base, void* stream) {
@@ -190,41 +234,79 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const sta
                            int64_t block_b, int64_t anchor_len, float scale,
                            const star_tensor* o, float* lse, void* stream) {
   int s;
-  if ((s = check_qkv(q, k, v)) != STAR_OK) return s;
-  if ((s = check_tensor(o, false)) != STAR_OK) return s;
-  if (k->S != q->S) return STAR_ERR_SHAPE;
-  if (o->B != q->B || o->H != q->H || o->S != q->S || o->D != q->D) return STAR_ERR_SHAPE;
-  if (block_b < 1 || anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
-  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if (anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
   if (q->S == 0) return STAR_OK;
   star::FlashParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.q = ref(q);
-  p.k = ref(k);
-  p.v = ref(v);
-  p.B = (int32_t)q->B;
-  p.Hq = (int32_t)q->H;
-  p.Hkv = (int32_t)k->H;
-  p.g = p.Hq / p.Hkv;
-  p.D = (int32_t)q->D;
-  p.in_f32 = q->dtype == STAR_F32;
-  p.q_rows = q->S;
-  p.kv_rows = k->S;
-  p.pos_shift = 0;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.mode = 0;
-  p.L = q->S;
-  p.b = block_b < q->S ? block_b : q->S;
+  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  p.pk = p.k;
+  p.pv = p.v;
+  p.pk_rows = k->S;
   p.a = anchor_len < p.b ? anchor_len : p.b;
   if (block_b >= q->S) p.a = 0;  // a single block has no anchor
-  p.o = o->data;
-  p.osB = o->sB;
-  p.osH = o->sH;
-  p.osS = o->sS;
-  p.lse = lse;
   return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_phase1_prefix(const star_tensor* q, const star_tensor* k, const star_tensor* v,
+                       const star_tensor* pk, const star_tensor* pv,
+                       const int64_t* prefix_start, const int64_t* prefix_len, int32_t nblocks,
+                       int64_t block_b, float scale, const star_tensor* o, float* lse,
+                       void* stream) {
+  int s;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if ((s = check_tensor(pk, true)) != STAR_OK) return s;
+  if ((s = check_tensor(pv, true)) != STAR_OK) return s;
+  if (pk->dtype != q->dtype || pv->dtype != q->dtype) return STAR_ERR_DTYPE;
+  if (pk->B != k->B || pk->H != k->H || pk->D != k->D) return STAR_ERR_SHAPE;
+  if (pv->B != k->B || pv->H != k->H || pv->D != k->D || pv->S != pk->S) return STAR_ERR_SHAPE;
+  const int64_t n = (q->S + block_b - 1) / block_b;
+  if (nblocks != n) return STAR_ERR_SHAPE;
+  if (n > STAR_MAX_PARTS) return STAR_ERR_UNSUPPORTED;
+  if (n > 0 && (prefix_start == nullptr || prefix_len == nullptr)) return STAR_ERR_NULL;
+  for (int64_t i = 0; i < n; ++i) {
+    if (prefix_start[i] < 0 || prefix_len[i] < 0) return STAR_ERR_SHAPE;
+    if (prefix_len[i] > pk->S - prefix_start[i]) return STAR_ERR_SHAPE;
+  }
+  if (q->S == 0) return STAR_OK;
+  star::FlashParams p;
+  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  p.pk = ref(pk);
+  p.pv = ref(pv);
+  p.pk_rows = pk->S;
+  p.prefix_tab = 1;
+  for (int64_t i = 0; i < n; ++i) {
+    p.offs[i] = prefix_start[i];
+    p.chunk[i] = prefix_len[i];
+  }
+  return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_gather_rows(const star_tensor* src, const int64_t* rows, const star_tensor* dst,
+                     void* stream) {
+  int s;
+  if ((s = check_tensor(src, true)) != STAR_OK) return s;
+  if ((s = check_tensor(dst, true)) != STAR_OK) return s;
+  if (dst->dtype != src->dtype) return STAR_ERR_DTYPE;
+  if (dst->B != src->B || dst->H != src->H || dst->D != src->D) return STAR_ERR_SHAPE;
+  if ((src->D * esize(src->dtype)) % 16) return STAR_ERR_ALIGN;
+  if (src->D > 1024) return STAR_ERR_UNSUPPORTED;
+  if (dst->S == 0) return STAR_OK;
+  if (rows == nullptr) return STAR_ERR_NULL;
+  star::GatherParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.src = ref(src);
+  p.dst = dst->data;
+  p.dsB = dst->sB;
+  p.dsH = dst->sH;
+  p.dsS = dst->sS;
+  p.rows = rows;
+  p.src_rows = src->S;
+  p.R = dst->S;
+  p.B = (int32_t)src->B;
+  p.H = (int32_t)src->H;
+  p.D = (int32_t)src->D;
+  p.f32 = src->dtype == STAR_F32;
+  return hip_status(star::launch_gather(p, (hipStream_t)stream));
 }
 
 int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
@@ -292,6 +374,9 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.mode = 1;
+  p.pk = p.k;            // key range A is empty in Phase 2
+  p.pv = p.v;
+  p.pk_rows = k_cache->S;
   p.P = P;
   p.splits = splits;
   for (int j = 0; j <= P; ++j) p.offs[j] = part_offsets[j];

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
   // ---- positions covered by this workgroup and by this wave
   const int64_t qlast = min(it.qr0 + p.m_pos, it.qr_end) - 1;
   const int64_t pmax = qlast + p.pos_shift;  // largest row position in the WG
-  it.ra1 = max(min(min(it.ra1, pmax + 1), p.kv_rows), it.ra0);
+  // range A (anchor / prefix) precedes every row: only its source bounds it
+  it.ra1 = max(min(it.ra1, p.pk_rows), it.ra0);
   it.rb1 = max(min(min(it.rb1, pmax + 1), p.kv_rows), it.rb0);
 
   int head[CB];
@@ -136,6 +137,10 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
                    (int64_t)it.kvh * p.k.sH;
   const T* vbase = reinterpret_cast<const T*>(p.v.data) + (int64_t)it.b * p.v.sB +
                    (int64_t)it.kvh * p.v.sH;
+  const T* pkbase = reinterpret_cast<const T*>(p.pk.data) + (int64_t)it.b * p.pk.sB +
+                    (int64_t)it.kvh * p.pk.sH;
+  const T* pvbase = reinterpret_cast<const T*>(p.pv.data) + (int64_t)it.b * p.pv.sB +
+                    (int64_t)it.kvh * p.pv.sH;
 
   const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
   const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
@@ -149,7 +154,14 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
     return t < nt0 ? ra0 + (int64_t)KT * t : rb0 + (int64_t)KT * (t - nt0);
   };
 
-  auto issue_loads = [&](int64_t kt) {
+  auto issue_loads = [&](int t) {
+    const bool A = t < nt0;
+    const int64_t kt = tile_start(t);
+    const int64_t rows = A ? p.pk_rows : p.kv_rows;
+    const T* kbs = A ? pkbase : kbase;
+    const T* vbs = A ? pvbase : vbase;
+    const int64_t kss = A ? p.pk.sS : p.k.sS;
+    const int64_t vss = A ? p.pv.sS : p.v.sS;
 #pragma unroll
     for (int i = 0; i < K_LOADS; ++i) {
       const int idx = tid + i * NT;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
       if (idx < K_UNITS) {
         const int r = idx / NCH, c = idx % NCH;
         const int64_t key = kt + r;
-        if (key < p.kv_rows) kst[i] = Load8<T>::load(kbase + key * p.k.sS + 8 * c);
+        if (key < rows) kst[i] = Load8<T>::load(kbs + key * kss + 8 * c);
       }
     }
 #pragma unroll
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t key = kt + 4 * kg + e;
-          if (key < p.kv_rows) vst[i][e] = Load8<T>::load(vbase + key * p.v.sS + 8 * dc);
+          if (key < rows) vst[i][e] = Load8<T>::load(vbs + key * vss + 8 * dc);
         }
       }
     }
@@ -216,26 +228,28 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
   const float c2 = p.scale_log2;
 
   if (nt > 0) {
-    issue_loads(tile_start(0));
+    issue_loads(0);
     store_lds(0);
   }
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
     const int64_t kt = tile_start(t);
-    if (t + 1 < nt) issue_loads(tile_start(t + 1));
+    if (t + 1 < nt) issue_loads(t + 1);
     const int buf = t & 1;
     const uint8_t* kb = smem + buf * KBYTES;
     const uint8_t* vb = smem + 2 * KBYTES + buf * KBYTES;
     const int64_t rend = t < nt0 ? ra1 : rb1;
 
-    if (kt <= wave_max) {
-      const bool need_mask = (kt + KT > rend) || (kt + KT - 1 > wave_min);
+    const bool A = t < nt0;       // range A: no position limit
+    if ((A && wave_max >= 0) || kt <= wave_max) {
+      const bool need_mask = (kt + KT > rend) || (!A && kt + KT - 1 > wave_min);
       // mask limits relative to the tile start, as 32-bit ints
       const int lim_end = (int)min(rend - kt, (int64_t)KT);
       int lim_pos[CB];
 #pragma unroll
-      for (int u = 0; u < CB; ++u) lim_pos[u] = (int)max(min(qpos[u] - kt, (int64_t)KT), (int64_t)-1);
+      for (int u = 0; u < CB; ++u)
+        lim_pos[u] = A ? KT : (int)max(min(qpos[u] - kt, (int64_t)KT), (int64_t)-1);
 #pragma unroll 1
       for (int kb2 = 0; kb2 < KT / 32; ++kb2) {
         f32x16 s[CB];

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 
   const int64_t qlast = min(it.qr0 + p.m_pos, it.qr_end) - 1;
   const int64_t pmax = qlast + p.pos_shift;
-  it.ra1 = max(min(min(it.ra1, pmax + 1), p.kv_rows), it.ra0);
+  // range A (anchor / prefix) precedes every row: only its source bounds it
+  it.ra1 = max(min(it.ra1, p.pk_rows), it.ra0);
   it.rb1 = max(min(min(it.rb1, pmax + 1), p.kv_rows), it.rb0);
 
   // this wave's column block: 32 consecutive positions of one query head
@@ -165,22 +166,41 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
                         (int64_t)it.kvh * p.k.sH;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v.data) + (int64_t)it.b * p.v.sB +
                         (int64_t)it.kvh * p.v.sH;
+  const __bf16* pkbase = reinterpret_cast<const __bf16*>(p.pk.data) + (int64_t)it.b * p.pk.sB +
+                         (int64_t)it.kvh * p.pk.sH;
+  const __bf16* pvbase = reinterpret_cast<const __bf16*>(p.pv.data) + (int64_t)it.b * p.pv.sB +
+                         (int64_t)it.kvh * p.pv.sH;
   int lrow[2], lcol[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     lrow[i] = 8 * wave + 4 * i + (lane >> 4);
     lcol[i] = 8 * ((lane & 15) ^ swz(lrow[i]));
   }
-  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it)
-  auto load_tile = [&](int buf, int64_t kt) {
-    const bool full = kt + KT <= p.kv_rows;
+  const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
+  const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
+  const int nsub = 2 * nt;                        // 32-key sub-tiles
+  auto tile_start = [&](int t) -> int64_t {
+    return t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0);
+  };
+
+  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it);
+  // rows past the source's end are clamped to its last row (masked later)
+  auto load_tile = [&](int buf, int t) {
+    const bool A = t < nt0;
+    const int64_t kt = tile_start(t);
+    const int64_t rows = A ? p.pk_rows : p.kv_rows;
+    const __bf16* kb = A ? pkbase : kbase;
+    const __bf16* vb = A ? pvbase : vbase;
+    const int64_t ks = A ? p.pk.sS : p.k.sS;
+    const int64_t vs = A ? p.pv.sS : p.v.sS;
+    const bool full = kt + KT <= rows;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int64_t key = kt + lrow[i];
-      if (!full) key = min(key, p.kv_rows - 1);
+      if (!full) key = min(key, rows - 1);
       const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(buf_ptr(buf) + (8 * wave + 4 * i) * ROWB));
-      dma16(kbase + key * p.k.sS + lcol[i], dk);
-      dma16(vbase + key * p.v.sS + lcol[i], dk + TILE);
+      dma16(kb + key * ks + lcol[i], dk);
+      dma16(vb + key * vs + lcol[i], dk + TILE);
     }
   };
 
@@ -191,13 +211,6 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m2 = -INFINITY, lsum = 0.f;
   const float c2 = p.scale_log2;
-
-  const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
-  const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
-  const int nsub = 2 * nt;                        // 32-key sub-tiles
-  auto tile_start = [&](int t) -> int64_t {
-    return t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0);
-  };
 
   // Sub-tile j (32 keys) lives in LDS buffer (j / 2) % 3, rows 32 (j % 2) ..
   // The loop below is unrolled over the 6 sub-tiles of one buffer cycle so
@@ -219,13 +232,15 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     const int t = j >> 1;
     return (t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0)) + 32 * (j & 1);
   };
-  // keys of sub-tile j past the range end or after the row's position -> -inf
+  // keys of sub-tile j past the range end or (range B only) after the row's
+  // position -> -inf
   auto mask = [&](int j, f32x16& s) {
     const int64_t ks = sub_key(j);
-    const int64_t rend = (j >> 1) < nt0 ? it.ra1 : it.rb1;
-    if (ks + 32 > rend || ks + 31 > wave_min) {
+    const bool A = (j >> 1) < nt0;
+    const int64_t rend = A ? it.ra1 : it.rb1;
+    if (ks + 32 > rend || (!A && ks + 31 > wave_min)) {
       const int lim_end = (int)min(rend - ks, (int64_t)32);
-      const int lim_pos = (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
+      const int lim_pos = A ? 32 : (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -235,8 +250,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   };
 
   // prologue: tiles 0 and 1 in flight, wait for tile 0, first S
-  if (nt > 0) load_tile(0, tile_start(0));
-  if (nt > 1) load_tile(1, tile_start(1));
+  if (nt > 0) load_tile(0, 0);
+  if (nt > 1) load_tile(1, 1);
   if (nt > 1) wait_vm_keep4(); else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 s = {};
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const int tn = (j >> 1) + 2;
-        if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tile_start(tn));
+        if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tn);
       }
     }
     // P_j = exp2(S_j c - m): fp32 for the denominator, bf16 for PV; issued

@@ -3,8 +3,12 @@
 //
 // Phase 1 (Pith review of Star Attention, "What carries the argument"): a
 // row of block i >= 1 sees the anchor keys [0, a) and its own block's keys
-// up to itself; block 1 is causal within itself.  Phase 2: each chunk of a
-// KV partition is one key range, visible to a row up to its position.
+// up to itself; block 1 is causal within itself.  With a prefix table the
+// anchor is replaced by any per-block list of rows that all precede the
+// block (the anchor ablations of the Star Attention pages; Pulsar's sink and
+// summaries, Pith review of Pulsar Attention, "What carries the argument").
+// Phase 2: each chunk of a KV partition is one key range, visible to a row
+// up to its position.
 #pragma once
 
 #include "common.h"
@@ -54,8 +58,13 @@ __device__ __forceinline__ void flash_get_item(const FlashParams& p, int lid, It
     const int64_t be = min(bs + p.b, p.L);
     it.qr0 = bs + (int64_t)j * p.m_pos;
     it.qr_end = be;
-    it.ra0 = 0;
-    it.ra1 = (blk > 0) ? p.a : 0;
+    if (p.prefix_tab) {
+      it.ra0 = p.offs[blk];
+      it.ra1 = p.offs[blk] + p.chunk[blk];
+    } else {
+      it.ra0 = 0;
+      it.ra1 = (blk > 0) ? p.a : 0;
+    }
     it.rb0 = bs;
     it.rb1 = be;
     it.cs = 0;

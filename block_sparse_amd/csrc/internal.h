@@ -15,9 +15,13 @@ struct TensorRef {
 };
 
 // Flash-style attention over analytic key ranges (Phase 1 and the Phase-2
-// query chunk).
+// query chunk).  Key range A (the anchor or prefix: every row sees all of
+// it) is read from pk/pv; key range B (own block or Phase-2 chunk, causal
+// by position) from k/v.
 struct FlashParams {
   TensorRef q, k, v;
+  TensorRef pk, pv;      // source of key range A (k/v themselves for the anchor)
+  int64_t pk_rows;       // rows of pk/pv
   int32_t B, Hq, Hkv, g;
   int32_t D;
   int32_t in_f32;        // Q/K/V are fp32 (rounded to bf16 on load)
@@ -34,10 +38,13 @@ struct FlashParams {
   // Phase 1
   int64_t L, b, a;
   int32_t nblocks, nqt_full, nqt_last, nqt0;
+  int32_t prefix_tab;    // 1: range A of block i is pk/pv rows [offs[i], offs[i] + chunk[i])
   // Phase 2
   int32_t P, splits, nqt2;
+  // Phase 2: partition offsets and split chunk length per partition.
+  // Phase 1 with prefix_tab: prefix start (offs) and length (chunk) per block.
   int64_t offs[STAR_MAX_PARTS + 1];
-  int64_t chunk[STAR_MAX_PARTS];  // split chunk length per partition
+  int64_t chunk[STAR_MAX_PARTS];
   // outputs
   void* o;               // Phase 1 O (bf16)
   int64_t osB, osH, osS;
@@ -122,5 +129,17 @@ struct MergeParams {
 };
 
 hipError_t launch_merge(MergeParams& p, hipStream_t stream);
+
+// dst[b, h, r] = src[b, h, rows[r]] (a zero row where rows[r] is out of range)
+struct GatherParams {
+  TensorRef src;
+  void* dst;
+  int64_t dsB, dsH, dsS;
+  const int64_t* rows;
+  int64_t src_rows, R;
+  int32_t B, H, D, f32;
+};
+
+hipError_t launch_gather(GatherParams& p, hipStream_t stream);
 
 }  // namespace star

@@ -13,6 +13,14 @@ review "What carries the argument"; atlas.scime.ai summary "Approach"):
            the LSE merge.  Then each generated token repeats the same with
            one row, attending to everything cached so far.
 
+Phase-1 variants (same cache afterwards, so Phase 2 is unchanged):
+  anchor at other position ids  the anchor's un-rotated keys re-rotated per
+           block at given positions (atlas.scime.ai summary, "Measured
+           effects reported in the paper");
+  Pulsar   a 64-token sink plus the Max-IDF summaries of every earlier block
+           at their original positions, gathered from the cache (Pith review
+           of Pulsar Attention, "What carries the argument").
+
 All buffers are caller-visible torch tensors; every computation runs in the
 library's kernels.
 """
@@ -22,8 +30,8 @@ import math
 
 import torch
 
-from . import (decode_prepare, kv_append, lse_merge, phase1_blocklocal, phase2_partial,
-               rope_apply)
+from . import (decode_prepare, gather_rows, kv_append, lse_merge, phase1_blocklocal,
+               phase1_prefix, phase2_partial, pulsar_prefix, rope_apply)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -97,6 +105,56 @@ class StarAttentionStep:
         L = self.L
         phase1_blocklocal(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
                           self.scale, out=self.o1, lse=self.lse1)
+
+    def pulsar_setup(self, tokens, m: int = 32, sink: int = 64, k: int = 16):
+        """Host-side Max-IDF selection for every sequence (``tokens[B, L]``)
+        and device buffers for the gathered prefix rows."""
+        self.pulsar = []
+        for bb in range(self.B):
+            rows, st, ln = pulsar_prefix(tokens[bb], self.L, self.b, m, sink, k)
+            R = max(int(rows.size), 1)
+            dev = self.qr.device
+            rows_d = torch.from_numpy(rows).to(dev)
+            pk = torch.empty((1, self.Hkv, R, self.D), dtype=torch.bfloat16, device=dev)
+            pv = torch.empty_like(pk)
+            self.pulsar.append((rows_d, st, ln, pk, pv))
+
+    def phase1_pulsar(self):
+        """Phase 1 with Pulsar's prefix: gather the sink and summary rows of
+        the rotated cache, then block-local attention over [prefix ; block]."""
+        L = self.L
+        for bb, (rows_d, st, ln, pk, pv) in enumerate(self.pulsar):
+            sl = slice(bb, bb + 1)
+            if rows_d.numel():
+                gather_rows(self.kc[sl, :, :L], rows_d, out=pk)
+                gather_rows(self.vc[sl, :, :L], rows_d, out=pv)
+            lse = None if self.lse1 is None else self.lse1[sl]
+            phase1_prefix(self.qr[sl], self.kc[sl, :, :L], self.vc[sl, :, :L], pk, pv, st, ln,
+                          self.b, self.scale, out=self.o1[sl], lse=lse)
+
+    def anchor_remap_setup(self, positions):
+        """Buffers for the anchor at other position ids: ``positions[i]``
+        (a ids each) are block i's anchor positions (block 0 unused)."""
+        n, a = self.P, self.a
+        dev = self.qr.device
+        self.apos = [torch.as_tensor(p, dtype=torch.int64).to(dev) for p in positions]
+        self.apk = torch.empty((self.B, self.Hkv, n * a, self.D), dtype=torch.bfloat16,
+                               device=dev)
+        self.apv = torch.empty_like(self.apk)
+        self.arows = torch.arange(a, dtype=torch.int64, device=dev).repeat(n)
+        self.ast = [i * a for i in range(n)]
+        self.aln = [0] + [a] * (n - 1)
+
+    def phase1_anchor_remap(self, k_pre):
+        """Phase 1 whose anchor keys (``k_pre[..., :a, :]``, un-rotated) are
+        rotated at each block's own anchor positions."""
+        L, a = self.L, self.a
+        for i in range(1, self.P):
+            rope_apply(k_pre[:, :, :a], pos=self.apos[i], base=self.base,
+                       out=self.apk[:, :, i * a:(i + 1) * a])
+        gather_rows(self.vc[:, :, :L], self.arows, out=self.apv)
+        phase1_prefix(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.apk, self.apv,
+                      self.ast, self.aln, self.b, self.scale, out=self.o1, lse=self.lse1)
 
     def query(self, qq, kq, vq):
         L, Lq = self.L, self.Lq

@@ -72,7 +72,8 @@ typedef struct {
   int64_t sB, sH, sS;
 } star_tensor;
 
-/* Largest number of KV partitions star_phase2_partial accepts. */
+/* Largest number of KV partitions star_phase2_partial accepts, and of
+   blocks star_phase1_prefix accepts. */
 #define STAR_MAX_PARTS 128
 /* Split chunks of a partition are whole multiples of this many keys. */
 #define STAR_SPLIT_ALIGN 64
@@ -152,6 +153,85 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
                            const star_tensor* v, int64_t block_b,
                            int64_t anchor_len, float scale,
                            const star_tensor* o, float* lse, void* stream);
+
+/*
+ * Phase 1 with an explicit per-block prefix in place of the anchor.
+ * Rows of block i (i = 0 .. nblocks-1, blocks as in
+ * star_phase1_blocklocal) attend to every row of
+ * [pk, pv][prefix_start[i], prefix_start[i] + prefix_len[i]) -- all of it,
+ * the prefix precedes the block -- and then to their own block's keys up to
+ * and including themselves.  The prefix rows are read, never output.
+ * This one form covers the variants the pages describe:
+ *  - the anchor itself: pk = k, pv = v, start 0, length a for i >= 1, 0 for
+ *    block 0 (what star_phase1_blocklocal computes);
+ *  - the anchor at other position ids (atlas.scime.ai summary, "Measured
+ *    effects reported in the paper"): the anchor keys re-rotated per block
+ *    (star_rope_apply with a position list) into pk;
+ *  - other anchor content (same ablation table): any rows in pk/pv;
+ *  - Pulsar's 64-token sink plus the Max-IDF summaries of all earlier
+ *    blocks, at their original position ids (Pith review of Pulsar
+ *    Attention, "What carries the argument"): rows gathered with
+ *    star_gather_rows, table from star_pulsar_prefix.
+ *
+ *   q, k, v        as for star_phase1_blocklocal (L = q->S = k->S).
+ *   pk, pv         [B, Hkv, R, D], same dtype as q (may be k and v).
+ *   prefix_start   host int64 [nblocks], prefix_len host int64 [nblocks]:
+ *                  0 <= start, 0 <= len, start + len <= R.
+ *   nblocks        must equal ceil(L / block_b), at most STAR_MAX_PARTS.
+ *   o, lse         as for star_phase1_blocklocal.
+ */
+int star_phase1_prefix(const star_tensor* q, const star_tensor* k,
+                       const star_tensor* v, const star_tensor* pk,
+                       const star_tensor* pv, const int64_t* prefix_start,
+                       const int64_t* prefix_len, int32_t nblocks,
+                       int64_t block_b, float scale, const star_tensor* o,
+                       float* lse, void* stream);
+
+/*
+ * Row gather: dst[b, h, r, :] = src[b, h, rows[r], :] for r < dst->S.  A
+ * row index outside [0, src->S) yields a zero row (no fault).  Used to
+ * assemble a prefix from context rows at their original positions (Pith
+ * review of Pulsar Attention, "What carries the argument": the sink and
+ * summary tokens keep their global position ids, so their rotated K/V are
+ * the context's own rows).
+ *
+ *   src   [B, H, S, D] bf16 or fp32.
+ *   rows  device int64 [dst->S] (may be NULL when dst->S == 0).
+ *   dst   [B, H, R, D], same B, H, D and dtype as src; must not overlap src.
+ */
+int star_gather_rows(const star_tensor* src, const int64_t* rows,
+                     const star_tensor* dst, void* stream);
+
+/*
+ * Pulsar's Phase-1 prefix (host-side integer work, no GPU call): Max-IDF
+ * chunk summaries and the per-block prefix table (Pith review of Pulsar
+ * Attention, "What carries the argument", "Core claim", "Assumptions & free
+ * parameters").  With n = ceil(L / block_b) blocks, df(t) = number of
+ * blocks containing token t and IDF(t) = log(n / max(df(t), 1)) (fp64):
+ *  - every block is cut into chunks of chunk_m tokens (the last may be
+ *    shorter); score(C) = max over t in C of IDF(t);
+ *  - summary i = the k best-scoring chunks of block i (equal scores: the
+ *    earlier chunk first), listed in positional order; in block 0 the chunks
+ *    that overlap the sink are not candidates;
+ *  - rows = [0, s) ++ summary 0 ++ ... ++ summary n-2, with s =
+ *    min(sink, block_b, L) the attention sink;
+ *  - block 0 has no prefix (prefix_len[0] = 0); block i >= 1 has
+ *    prefix_start[i] = 0 and prefix_len[i] = s + |summary 0| + ... +
+ *    |summary i-1|: the sink and the summaries of all earlier blocks.
+ *
+ *   tokens        host int32 [L] token ids.
+ *   rows          host int64 [rows_cap] output; *n_rows receives the count.
+ *                 If rows_cap is too small, *n_rows is set to the count
+ *                 needed and STAR_ERR_SHAPE is returned.
+ *   prefix_start, prefix_len  host int64 [nblocks] outputs;
+ *                 nblocks must equal n.
+ * chunk_m >= 1, sink >= 0, k >= 0.
+ */
+int star_pulsar_prefix(const int32_t* tokens, int64_t L, int64_t block_b,
+                       int32_t chunk_m, int32_t sink, int32_t k,
+                       int64_t* rows, int64_t rows_cap, int64_t* n_rows,
+                       int64_t* prefix_start, int64_t* prefix_len,
+                       int32_t nblocks);
 
 /*
  * Phase 2 partials: local attention of query rows over each KV partition.

@@ -1,7 +1,8 @@
 """Helpers shared by the GPU parity tests (not collected by pytest).
 
 Tolerances (from the method's numeric contract: bf16 in, fp32 accumulate):
-attention outputs max-abs <= 1e-2 and mean-abs <= 1e-3, log-sum-exp values
+attention outputs max-abs <= 1e-2 (plus, for outputs stored in bf16, the
+bf16 rounding of the value itself) and mean-abs <= 1e-3, log-sum-exp values
 |d| <= 1e-3, and no NaN/Inf anywhere.
 """
 import math
@@ -38,12 +39,19 @@ def rand_tensor(seed, tid, B, H, S, D, scale=1.0, bf16=True):
 
 
 def check_out(got: np.ndarray, ref: np.ndarray, what: str,
-              max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS):
+              max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS, bf16_out=False):
+    """Element-wise max-abs and overall mean-abs bounds.  For a bf16 output
+    (Phase-1 O) the bound on an element also admits the rounding of that
+    output to bf16, at most 2^-8 |ref| (half an ulp, relative to the value):
+    a stored bf16 value of magnitude above ~2.5 cannot be within 1e-2 of
+    the exact result."""
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = np.abs(got - ref)
+    lim = max_abs + (2.0 ** -8) * np.abs(ref) if bf16_out else max_abs
     mx, mn = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
-    assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+    ok = bool((err <= lim).all())
+    assert ok and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
     return mx, mn
 
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 100
+    assert lib.star_abi_version() == 200
 
 
 def test_status_strings(lib):
@@ -138,3 +138,90 @@ def test_merge_rope_append_validation(lib):
     assert dp(T(B=1, H=8, S=2, D=128), T(B=1, H=8, S=2, D=128)) == -2
     assert dp(qn, qo, slot=8) == -2
     assert dp(T(B=1, H=8, S=3, D=128, data=0), qo) == -1
+
+
+def test_phase1_prefix_validation(lib):
+    ok = dict(B=1, H=2, S=64, D=64)
+    q, o = T(**ok), T(**ok)
+    k, v = T(B=1, H=1, S=64, D=64), T(B=1, H=1, S=64, D=64)
+    pk, pv = T(B=1, H=1, S=10, D=64), T(B=1, H=1, S=10, D=64)
+
+    def pp(pk=pk, pv=pv, st=(0, 0, 0, 0), ln=(0, 5, 5, 10), n=None, b=16, q=q):
+        n = len(st) if n is None else n
+        sa = (ctypes.c_int64 * len(st))(*st)
+        la = (ctypes.c_int64 * len(ln))(*ln)
+        return lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                      ctypes.byref(pk), ctypes.byref(pv), sa, la, n, b, 0.1,
+                                      ctypes.byref(o), None, None)
+    assert pp(ln=(0, 5, 5, 11)) == -2                  # past the prefix rows
+    assert pp(st=(0, 0, 6, 0)) == -2                   # 6 + 5 > 10
+    assert pp(st=(0, -1, 0, 0)) == -2
+    assert pp(ln=(0, -1, 0, 0)) == -2
+    assert pp(n=3) == -2                               # table size != ceil(L/b)
+    assert pp(pk=T(B=1, H=1, S=10, D=64, dtype=1)) == -3
+    assert pp(pv=T(B=1, H=1, S=11, D=64)) == -2        # pk/pv rows differ
+    assert pp(pk=T(B=1, H=2, S=10, D=64), pv=T(B=1, H=2, S=10, D=64)) == -2
+    assert pp(pk=T(B=1, H=1, S=10, D=64, data=FAKE + 8)) == -4
+    st = [0] * 129
+    assert pp(st=st, ln=st, b=1, q=T(B=1, H=2, S=129, D=64)) == -2   # k has 64 rows
+    assert lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                  ctypes.byref(pk), ctypes.byref(pv), None, None, 4, 16, 0.1,
+                                  ctypes.byref(o), None, None) == -1
+    z = dict(B=1, S=0, D=64)
+    assert lib.star_phase1_prefix(ctypes.byref(T(H=2, **z)), ctypes.byref(T(H=1, **z)),
+                                  ctypes.byref(T(H=1, **z)), ctypes.byref(pk), ctypes.byref(pv),
+                                  None, None, 0, 16, 0.1, ctypes.byref(T(H=2, **z)), None,
+                                  None) == 0
+
+
+def test_phase1_prefix_too_many_blocks(lib):
+    L, b = 1290, 10                                    # 129 blocks
+    q, o = T(B=1, H=2, S=L, D=64), T(B=1, H=2, S=L, D=64)
+    k, v = T(B=1, H=1, S=L, D=64), T(B=1, H=1, S=L, D=64)
+    z = (ctypes.c_int64 * 129)(*([0] * 129))
+    assert lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                  ctypes.byref(k), ctypes.byref(v), z, z, 129, b, 0.1,
+                                  ctypes.byref(o), None, None) == -5
+
+
+def test_gather_validation(lib):
+    src, dst = T(B=1, H=2, S=50, D=128), T(B=1, H=2, S=7, D=128)
+    g = lambda s=src, d=dst, rows=FAKE: lib.star_gather_rows(ctypes.byref(s), rows,
+                                                             ctypes.byref(d), None)
+    assert g(rows=None) == -1
+    assert g(d=T(B=1, H=2, S=7, D=128, dtype=1)) == -3
+    assert g(d=T(B=1, H=3, S=7, D=128)) == -2
+    assert g(d=T(B=1, H=2, S=7, D=64)) == -2
+    assert g(d=T(B=1, H=2, S=0, D=128), rows=None) == 0
+
+
+def test_pulsar_prefix_host_matches_oracle(lib):
+    """The library's host-side Max-IDF selection equals the oracle's,
+    index for index (integer work: bit-exact), on Zipf-distributed token
+    ids at three block shapes, including a ragged tail and b % 32 != 0."""
+    import numpy as np
+
+    import block_sparse_amd as sa
+    import oracle.star_oracle as so
+    from workloads import token_ids
+    for (L, b, m, sink, k) in [(16384, 4096, 32, 64, 16), (5000, 700, 32, 64, 5),
+                               (2048, 100, 24, 40, 3), (300, 400, 32, 64, 2)]:
+        tok = token_ids(7, 1, L)[0]
+        r1, s1, l1 = sa.pulsar_prefix(tok, L, b, m, sink, k)
+        r2, s2, l2 = so.pulsar_prefix(tok, L, b, m, sink, k)
+        assert np.array_equal(r1, r2) and np.array_equal(s1, s2) and np.array_equal(l1, l2)
+
+
+def test_pulsar_prefix_host_validation(lib):
+    import numpy as np
+    tok = np.zeros(100, dtype=np.int32)
+    tp = tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    n = ctypes.c_int64(0)
+    a = (ctypes.c_int64 * 4)()
+    P = lambda L=100, b=25, m=32, s=64, k=1, rows=None, cap=0, nb=4, nr=ctypes.byref(n): \
+        lib.star_pulsar_prefix(tp, L, b, m, s, k, rows, cap, nr, a, a, nb)
+    assert P(nr=None) == -1
+    assert P(b=0) == -2 and P(m=0) == -2 and P(k=-1) == -2 and P(nb=3) == -2
+    assert P(cap=0) == -2 and n.value > 0            # too small: reports the size
+    rows = (ctypes.c_int64 * n.value)()
+    assert P(rows=rows, cap=n.value) == 0

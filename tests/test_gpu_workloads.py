@@ -9,7 +9,9 @@ by one from the raw seeded inputs:
     of every block; for llama8b-16k every row of those heads;
   * Phase 2: every query row and every decode step of the checked heads;
 and on properties that hold at any size (every Phase-1 output and lse of
-every head finite).
+every head finite).  The Phase-1 variants (Pulsar's sink + Max-IDF summaries,
+the anchor at other position ids) are checked the same way at the 8B-128K
+and 70B-64K shapes.
 """
 import math
 import time
@@ -45,7 +47,7 @@ def test_tiny_full(bf16):
     o2, l2 = sa.lse_merge(op, lp)
     torch.cuda.synchronize()
     ref = so.star_attention(w, {n: as_f64(t) for n, t in x.items()})
-    check_out(host64(o1), ref["O1"], "phase1 O")
+    check_out(host64(o1), ref["O1"], "phase1 O", bf16_out=True)
     check_lse(host64(l1), ref["LSE1"], "phase1 LSE")
     check_out(host64(op), ref["P2o"], "phase2 partials")
     check_lse(host64(lp), ref["P2l"], "phase2 partial lse")
@@ -114,7 +116,7 @@ def test_llama_workload(name):
                 ro, rl = so.phase1_rows(qrows, pos, K, V, w.b, w.a, scale)
                 go = host64(st.o1[bb, h].index_select(0, pos_t))
                 gl = host64(st.lse1[bb, h].index_select(0, pos_t))
-                e1 = check_out(go, ro, f"{name} phase1 O b{bb} h{h}")
+                e1 = check_out(go, ro, f"{name} phase1 O b{bb} h{h}", bf16_out=True)
                 e2 = check_lse(gl, rl, f"{name} phase1 LSE b{bb} h{h}")
                 # query rows and every decode step, against global attention
                 qq = rot(f64(x["qq"][bb, h]), pos_q)
@@ -130,3 +132,65 @@ def test_llama_workload(name):
                                     (e1[0], e2, e3[0], e4, e5[0], e6)):
                     worst[key] = max(worst.get(key, 0.0), val)
     log(f"{name}: worst max-abs errors {worst} over {pos.size} rows/head")
+
+
+# Phase-1 variants at full size: (workload, variant, checked KV heads)
+VARIANTS = [("llama8b-128k", "pulsar", (0, 7)), ("llama8b-128k", "anchor_remap", (2,)),
+            ("llama70b-64k", "pulsar", (5,))]
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("name,variant,kv_heads", VARIANTS,
+                         ids=[f"{n}-{v}" for n, v, _ in VARIANTS])
+def test_llama_phase1_variants(name, variant, kv_heads):
+    """Pulsar's prefix and the anchor at other position ids, at the
+    workloads' full shapes, on sampled rows of the checked heads."""
+    from workloads import anchor_positions, pulsar_params, token_ids
+    w = WORKLOADS[name]
+    g = w.g
+    scale = 1.0 / math.sqrt(w.D)
+    log(f"{name} {variant}: generating inputs")
+    x = inputs(w, as_bf16=True)
+    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, 0, 0, rope=True, base=w.base)
+    st.load_context(to_dev(x["v"]))
+    kdev = to_dev(x["k"])
+    st.rope_context(to_dev(x["q"]), kdev)
+    pp = pulsar_params(w)
+    tok = token_ids(w.seed, w.B, w.L)
+    apos = anchor_positions(w.seed, w.L, w.b, w.a)
+    log(f"{name} {variant}: GPU pass")
+    if variant == "pulsar":
+        st.pulsar_setup(tok, pp.m, pp.sink, pp.k)
+        st.phase1_pulsar()
+    else:
+        st.anchor_remap_setup(apos)
+        st.phase1_anchor_remap(kdev)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(st.o1).all()) and bool(torch.isfinite(st.lse1).all())
+    pos = sample_rows(w, 16, w.seed + 100)
+    pos_t = torch.from_numpy(pos).cuda()
+    rot = lambda t, p: so.round_bf16(so.rope(t, p, w.base))
+    worst = [0.0, 0.0]
+    for bb in range(w.B):
+        if variant == "pulsar":
+            rows, pst, pln = so.pulsar_prefix(tok[bb], w.L, w.b, pp.m, pp.sink, pp.k)
+        for kvh in kv_heads:
+            log(f"{name} {variant}: oracle b={bb} kv head {kvh}")
+            K = rot(f64(x["k"][bb, kvh]), np.arange(w.L))
+            V = f64(x["v"][bb, kvh])
+            if variant == "pulsar":
+                PK, PV = K[rows], V[rows]
+            else:
+                PK = so.remapped_anchor(f64(x["k"][bb, kvh]), apos, w.base)
+                PV = np.concatenate([V[:w.a]] * len(apos))
+                pst = np.arange(len(apos)) * w.a
+                pln = np.array([0] + [w.a] * (len(apos) - 1))
+            for h in range(kvh * g, (kvh + 1) * g):
+                qrows = rot(f64(x["q"][bb, h][pos]), pos)
+                ro, rl = so.phase1_prefix_rows(qrows, pos, K, V, PK, PV, pst, pln, w.b, scale)
+                e1 = check_out(host64(st.o1[bb, h].index_select(0, pos_t)), ro,
+                               f"{name} {variant} O b{bb} h{h}", bf16_out=True)
+                e2 = check_lse(host64(st.lse1[bb, h].index_select(0, pos_t)), rl,
+                               f"{name} {variant} LSE b{bb} h{h}")
+                worst = [max(worst[0], e1[0]), max(worst[1], e2)]
+    log(f"{name} {variant}: worst O {worst[0]:.3e} LSE {worst[1]:.3e} over {pos.size} rows/head")

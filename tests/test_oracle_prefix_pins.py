@@ -247,3 +247,16 @@ def test_pulsar_planted_mistake_is_caught():
     wrong = min(math.log(4 / max(df.get(int(x), 0), 1)) for x in t[192:224])
     right = so.maxidf_score(t[192:224], df, 4)
     assert wrong == 0.0 and right == math.log(4)
+
+
+def test_pulsar_16k_prefix_is_1600_entries():
+    """At 16K with 4 hosts, 16 chunks of 32 per block: the last host's
+    prefix (sink + 3 summaries) is the 1,600 entries the Pulsar review
+    speaks of, and its Phase-1 length is L/4 + 1600."""
+    g = json.load(open(os.path.join(GOLD, "pulsar_lengths.json")))["fixed_budget_16k"]
+    L, hosts = g["L"], g["hosts"]
+    b = L // hosts
+    t = np.random.default_rng(26).integers(0, 5000, size=L)
+    rows, st, ln = so.pulsar_prefix(t, L, b, m=32, sink=64, k=g["summary_tokens"] // 32)
+    assert rows.size == ln[-1] == g["prefix_entries_last_host"]
+    assert so.pulsar_host_length(L, b, 64, g["summary_tokens"], hosts - 1) == L // 4 + 1600
