@@ -70,11 +70,14 @@ def pmc_traffic():
     return float(t.group(1)) if m.group(1) == cur else None
 
 
-def cpu_baseline(w, x):
+def cpu_baseline(w, x, heads: int = 4, rows_per_call: int = 4096):
     """Time the CPU oracle (as it stands) on a bounded sample of Phase 1:
-    the last ``rows`` rows of block 2 of query head 0, batch 0 (anchor plus
-    a long causal prefix).  Scaled to whole-workload context tokens/s by the
-    ratio of useful (query, key) pairs."""
+    every row of block 2 (anchor plus its causal prefix) for the first
+    ``heads`` query heads of batch 0 (one GQA group: they share KV head 0),
+    in calls of ``rows_per_call`` rows, including the RoPE of the sampled
+    rows and of that KV head.  About 10-15 s on 16 host threads at the
+    8B-128K shape.  Scaled to whole-workload context tokens/s by the ratio
+    of useful (query, key) pairs."""
     import numpy as np
 
     import oracle.star_oracle as so
@@ -88,25 +91,81 @@ def cpu_baseline(w, x):
     blk = 1 if w.L > w.b else 0
     s = blk * w.b
     e = min(s + w.b, w.L)
-    rows = min(4096, e - s)
-    pos = np.arange(e - rows, e)
+    heads = min(heads, w.g)
     t0 = time.perf_counter()
     kv = 0
     K = so.rope(as_f64(x["k"][0, kv]), np.arange(w.L), w.base) if w.rope else as_f64(x["k"][0, kv])
     V = as_f64(x["v"][0, kv])
-    q = as_f64(x["q"][0, 0][pos])
-    q = so.rope(q, pos, w.base) if w.rope else q
-    so.phase1_rows(q, pos, K, V, w.b, w.a, scale)
+    for h in range(heads):
+        for r0 in range(s, e, rows_per_call):
+            pos = np.arange(r0, min(r0 + rows_per_call, e))
+            q = as_f64(x["q"][0, h][pos])
+            q = so.rope(q, pos, w.base) if w.rope else q
+            so.phase1_rows(q, pos, K, V, w.b, w.a, scale)
     dt = time.perf_counter() - t0
-    sample_pairs = sum((w.a if blk > 0 else 0) + (p - s + 1) for p in pos)
+    sample_pairs = heads * sum((w.a if blk > 0 else 0) + (p - s + 1) for p in range(s, e))
     total_pairs = phase1_pairs(w.L, w.b, w.a) * w.Hq * w.B
     tokens_per_s = w.B * w.L / (dt * total_pairs / sample_pairs)
     return {"value": tokens_per_s, "unit": "context tokens/s (Phase 1, extrapolated)",
             "cores": int(cores), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, Phase 1 of {rows} rows (positions {pos[0]}-{pos[-1]}, "
-                       f"block {blk + 1}) of one query head, incl. RoPE of that KV head; "
-                       f"{dt:.1f} s; scaled by useful (q,k) pairs {sample_pairs:.3e} of "
+            "sample": (f"fp64 numpy oracle, Phase 1 of all {e - s} rows of block {blk + 1} "
+                       f"(positions {s}-{e - 1}) for {heads} query heads of KV head 0, incl. "
+                       f"RoPE; {dt:.1f} s; scaled by useful (q,k) pairs {sample_pairs:.3e} of "
                        f"{total_pairs:.3e}")}
+
+
+def prefix_pairs(L: int, b: int, lens) -> int:
+    """Useful (query, key) pairs per head of Phase 1 with a per-block prefix
+    of lens[i] keys: every row sees its block's prefix and its causal
+    prefix within the block."""
+    tot = 0
+    for i, s in enumerate(range(0, L, b)):
+        n = min(s + b, L) - s
+        tot += n * (n + 1) // 2 + int(lens[i]) * n
+    return tot
+
+
+def phase1_variants(st, dev, w, x, ev, reps=3):
+    """Phase-1 time of the prefix variants on the same context (after the
+    timed region): Pulsar's sink + Max-IDF summaries (gather + prefix
+    attention; the host-side selection runs once, before timing) and the
+    anchor re-rotated at other position ids (per-block RoPE of the anchor
+    keys + gather of the anchor values + prefix attention)."""
+    import numpy as np
+    import torch
+
+    from workloads import anchor_positions, pulsar_params, token_ids
+    out = {}
+    pp = pulsar_params(w)
+    t0 = time.perf_counter()
+    st.pulsar_setup(token_ids(w.seed, w.B, w.L), pp.m, pp.sink, pp.k)
+    sel_ms = (time.perf_counter() - t0) * 1e3
+    st.anchor_remap_setup(anchor_positions(w.seed, w.L, w.b, w.a))
+    runs = {"pulsar": st.phase1_pulsar, "anchor_random_positions": lambda: st.phase1_anchor_remap(dev["k"])}
+    for name, fn in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        e = [(ev(), ev()) for _ in range(reps)]
+        for e0, e1 in e:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in e]))
+        if name == "pulsar":
+            pairs = sum(prefix_pairs(w.L, w.b, ln) for (_, _, ln, _, _) in st.pulsar) * w.Hq
+            extra = {"prefix_rows_last_block": int(st.pulsar[0][2][-1]),
+                     "host_selection_ms": sel_ms,
+                     "params": {"chunk": pp.m, "sink": pp.sink, "chunks_per_block": pp.k}}
+        else:
+            pairs = prefix_pairs(w.L, w.b, st.aln) * w.Hq * w.B
+            extra = {}
+        fl = 4.0 * w.D * pairs
+        out[name] = {"ms": ms, "context_tokens_per_s": w.B * w.L / (ms * 1e-3),
+                     "tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_flops": fl, **extra}
+    # the Star Phase 1 leaves o1 as the timed pass did: restore it
+    st.phase1()
+    return out
 
 
 def decode_cold(st, dev, w, ev, samples=16):
@@ -125,7 +184,7 @@ def decode_cold(st, dev, w, ev, samples=16):
     ts = sorted(set(np.linspace(0, w.T - 1, min(samples, w.T)).astype(int).tolist()))
     recs = []
     for i, t in enumerate(ts):
-        torch.sum(flush, dtype=torch.float32, out=sink)
+        torch.sum(flush, dim=0, out=sink)
         e0, e1 = ev(), ev()
         e0.record()
         st.decode(t, dev["qd"][:, :, t:t + 1], dev["kd"][:, :, t:t + 1],
@@ -150,6 +209,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b-128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache decode timing")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the Phase-1 prefix variants (Pulsar, anchor positions)")
     ap.add_argument("--splits-decode", type=int, default=None,
                     help="chunks per KV partition for the decode partials")
     ap.add_argument("--splits-query", type=int, default=None,
@@ -253,8 +316,10 @@ def main():
                          "frac_of_hbm_peak": byts / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "note": "whole decode step (RoPE, KV append, partials, merge), "
                                  "K+V bytes of every visible token"}
-    if not args.phase1_only and w.T > 0:
+    if not args.phase1_only and w.T > 0 and not args.no_cold:
         out["decode_cold"] = decode_cold(st, dev, w, ev)
+    if w.rope and not args.no_variants:
+        out["phase1_variants"] = phase1_variants(st, dev, w, x, ev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)
