@@ -61,16 +61,17 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// global -> LDS DMA of 16 bytes per lane: lane i's bytes land at LDS address
-// lds + 16 i.  Issued from inline asm (inputs only: the address VGPRs are
-// read at issue, M0 is set in the same block) so that the compiler does not
-// treat it as a possibly-aliasing LDS store and wait for it before every
-// later LDS read; the kernel waits for it explicitly (vmcnt(0) + barrier)
-// before any wave reads the buffer.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// global -> LDS DMA of 16 bytes per lane from base + off (base scalar, off
+// a per-lane 32-bit byte offset): lane i's bytes land at LDS address
+// lds + 16 i.  Issued from inline asm (inputs only: the offset VGPR and
+// base SGPRs are read at issue, M0 is set in the same block) so that the
+// compiler does not treat it as a possibly-aliasing LDS store and wait for
+// it before every later LDS read; the kernel waits for it explicitly
+// (vmcnt(0) + barrier) before any wave reads the buffer.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(lds)
+               : "v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
@@ -161,21 +162,33 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   }
 
   // ---- direct global -> LDS loads: wave w fills rows 8w .. 8w+7 of the
-  // K and V tiles, 4 rows (1 KiB) per instruction
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k.data) + (int64_t)it.b * p.k.sB +
-                        (int64_t)it.kvh * p.k.sH;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v.data) + (int64_t)it.b * p.v.sB +
-                        (int64_t)it.kvh * p.v.sH;
-  const __bf16* pkbase = reinterpret_cast<const __bf16*>(p.pk.data) + (int64_t)it.b * p.pk.sB +
-                         (int64_t)it.kvh * p.pk.sH;
-  const __bf16* pvbase = reinterpret_cast<const __bf16*>(p.pv.data) + (int64_t)it.b * p.pv.sB +
-                         (int64_t)it.kvh * p.pv.sH;
-  int lrow[2], lcol[2];
+  // K and V tiles, 4 rows (1 KiB) per instruction.  A lane's byte offset
+  // inside a tile is fixed (per key range, as the strides may differ); the
+  // tile's base address is scalar, so a full tile costs no VALU work.
+  const int64_t ksA = p.pk.sS * 2, vsA = p.pv.sS * 2;     // bytes per row
+  const int64_t ksB = p.k.sS * 2, vsB = p.v.sS * 2;
+  const uint8_t* kbA = reinterpret_cast<const uint8_t*>(p.pk.data) +
+                       ((int64_t)it.b * p.pk.sB + (int64_t)it.kvh * p.pk.sH) * 2 + it.ra0 * ksA;
+  const uint8_t* vbA = reinterpret_cast<const uint8_t*>(p.pv.data) +
+                       ((int64_t)it.b * p.pv.sB + (int64_t)it.kvh * p.pv.sH) * 2 + it.ra0 * vsA;
+  const uint8_t* kbB = reinterpret_cast<const uint8_t*>(p.k.data) +
+                       ((int64_t)it.b * p.k.sB + (int64_t)it.kvh * p.k.sH) * 2 + it.rb0 * ksB;
+  const uint8_t* vbB = reinterpret_cast<const uint8_t*>(p.v.data) +
+                       ((int64_t)it.b * p.v.sB + (int64_t)it.kvh * p.v.sH) * 2 + it.rb0 * vsB;
+  // rows of each range that stay inside its source tensor
+  const int64_t rowsA = p.pk_rows - it.ra0, rowsB = p.kv_rows - it.rb0;
+  int lrow[2], lcolb[2];
+  uint32_t okA[2], ovA[2], okB[2], ovB[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     lrow[i] = 8 * wave + 4 * i + (lane >> 4);
-    lcol[i] = 8 * ((lane & 15) ^ swz(lrow[i]));
+    lcolb[i] = 16 * ((lane & 15) ^ swz(lrow[i]));
+    okA[i] = (uint32_t)(lrow[i] * ksA + lcolb[i]);
+    ovA[i] = (uint32_t)(lrow[i] * vsA + lcolb[i]);
+    okB[i] = (uint32_t)(lrow[i] * ksB + lcolb[i]);
+    ovB[i] = (uint32_t)(lrow[i] * vsB + lcolb[i]);
   }
+
   const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
   const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
   const int nsub = 2 * nt;                        // 32-key sub-tiles
@@ -183,25 +196,31 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     return t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0);
   };
 
-  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it);
-  // rows past the source's end are clamped to its last row (masked later)
-  auto load_tile = [&](int buf, int t) {
-    const bool A = t < nt0;
-    const int64_t kt = tile_start(t);
-    const int64_t rows = A ? p.pk_rows : p.kv_rows;
-    const __bf16* kb = A ? pkbase : kbase;
-    const __bf16* vb = A ? pvbase : vbase;
-    const int64_t ks = A ? p.pk.sS : p.k.sS;
-    const int64_t vs = A ? p.pv.sS : p.v.sS;
-    const bool full = kt + KT <= rows;
+  // the 4 DMAs of one tile whose first row is r0 rows into its range; rows
+  // past the source's end (last tile only) are clamped to its last row and
+  // masked later
+  auto issue = [&](int buf, const uint8_t* kb, const uint8_t* vb, int64_t ks, int64_t vs,
+                   const uint32_t* ok, const uint32_t* ov, int64_t r0, int64_t rows) {
+    kb += r0 * ks;
+    vb += r0 * vs;
+    const bool full = r0 + KT <= rows;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int64_t key = kt + lrow[i];
-      if (!full) key = min(key, rows - 1);
       const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(buf_ptr(buf) + (8 * wave + 4 * i) * ROWB));
-      dma16(kb + key * ks + lcol[i], dk);
-      dma16(vb + key * vs + lcol[i], dk + TILE);
+      uint32_t okk = ok[i], ovv = ov[i];
+      if (!full) {
+        const int64_t rr = min(r0 + lrow[i], rows - 1) - r0;
+        okk = (uint32_t)(rr * ks + lcolb[i]);
+        ovv = (uint32_t)(rr * vs + lcolb[i]);
+      }
+      dma16(kb, okk, dk);
+      dma16(vb, ovv, dk + TILE);
     }
+  };
+  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it)
+  auto load_tile = [&](int buf, int t) {
+    if (t < nt0) issue(buf, kbA, vbA, ksA, vsA, okA, ovA, (int64_t)KT * t, rowsA);
+    else issue(buf, kbB, vbB, ksB, vsB, okB, ovB, (int64_t)KT * (t - nt0), rowsB);
   };
 
   f32x16 oacc[D / 32];
@@ -210,6 +229,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m2 = -INFINITY, lsum = 0.f;
+  float msub = 0.f;          // m2 where finite, else 0 (the exp2 shift)
   const float c2 = p.scale_log2;
 
   // Sub-tile j (32 keys) lives in LDS buffer (j / 2) % 3, rows 32 (j % 2) ..
@@ -279,7 +299,10 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     const bool need = mt2 > m2 + kRescaleLog2;
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
-      if (need) m2 = mt2;
+      if (need) {
+        m2 = mt2;
+        msub = mt2;
+      }
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -300,7 +323,6 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     // P_j = exp2(S_j c - m): fp32 for the denominator, bf16 for PV; issued
     // together with the next sub-tile's QK MFMAs (unconditional so they
     // share a basic block; after the last sub-tile the result is unused)
-    const float msub = (m2 == -INFINITY) ? 0.f : m2;
     bf16x8 pf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -375,7 +397,14 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 
 }  // namespace
 
-bool flash2_supported(const FlashParams& p) { return p.D == 128 && !p.in_f32; }
+// The tile DMAs address a lane's bytes with a 32-bit offset from a scalar
+// base: 64 rows of every source must span less than 2 GiB.
+bool flash2_supported(const FlashParams& p) {
+  const int64_t lim = (int64_t)1 << 31;
+  for (int64_t s : {p.k.sS, p.v.sS, p.pk.sS, p.pv.sS})
+    if (s * 2 * 64 >= lim) return false;
+  return p.D == 128 && !p.in_f32;
+}
 
 hipError_t launch_flash2(FlashParams& p, hipStream_t stream) {
   if (!flash_geometry(p, NW)) return hipErrorInvalidValue;
