@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
 __all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_prefix",
-           "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "split_ranges",
+           "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
+           "split_ranges",
            "StarError", "library"]
 
 
@@ -252,4 +253,33 @@ def lse_merge(o_part, lse_part, out=None, lse=None, out_dtype=torch.float32,
     st = library().star_lse_merge(_ptr(o_part), _ptr(lse_part), int(N), ctypes.byref(do),
                                   _ptr(lse), _stream(o_part))
     _lib.check("star_lse_merge", st)
+    return out, lse
+
+
+def decode_step(q_new, k_new, v_new, k_cache, v_cache, slot: int, pos: int, part_offsets,
+                splits: int, o_part, lse_part, out, lse=None, base: float = 500000.0,
+                rope: bool = True, scale: float | None = None):
+    """One generated token: rope of its q/k at ``pos``, its K/V appended at
+    cache row ``slot`` and the split-KV partials over ``part_offsets`` in one
+    launch, then their merge into ``out[B, Hq, 1, D]`` (and ``lse`` [B, Hq]).
+    ``o_part``/``lse_part`` are fp32 workspaces of phase2_partial's sizes."""
+    B, Hq, _, D = q_new.shape
+    P = len(part_offsets) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    N = P * splits
+    for t, n in ((o_part, N * B * Hq * D), (lse_part, N * B * Hq)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+            raise ValueError("o_part / lse_part must be contiguous fp32 buffers of the full size")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq] tensor")
+    offs = (ctypes.c_int64 * (P + 1))(*[int(x) for x in part_offsets])
+    d = [_desc(t) for t in (q_new, k_new, v_new, k_cache, v_cache)]
+    do = _desc(out)
+    st = library().star_decode_step(*[ctypes.byref(x) for x in d], int(slot), int(pos),
+                                    float(base), int(bool(rope)), offs, int(P), int(splits),
+                                    float(scale), _ptr(o_part), _ptr(lse_part),
+                                    ctypes.byref(do), _ptr(lse), _stream(q_new))
+    _lib.check("star_decode_step", st)
     return out, lse

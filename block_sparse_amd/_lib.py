@@ -26,7 +26,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 # every symbol include/star_attn.h declares
 EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase1_prefix", "star_gather_rows", "star_pulsar_prefix",
-           "star_phase2_partial", "star_lse_merge", "star_status_string",
+           "star_phase2_partial", "star_lse_merge", "star_decode_step", "star_status_string",
            "star_abi_version")
 
 
@@ -59,6 +59,8 @@ _SIGS = {
     "star_phase2_partial": (ctypes.c_int, [_T, _T, _T, _P(_i64), _i32, _i32, _i64, _f32,
                                            _vp, _vp, _vp]),
     "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _T, _vp, _vp]),
+    "star_decode_step": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _P(_i64), _i32,
+                                        _i32, _f32, _vp, _vp, _T, _vp, _vp]),
     "star_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "star_abi_version": (ctypes.c_int, []),
 }

@@ -58,6 +58,52 @@ int check_qkv(const star_tensor* q, const star_tensor* k, const star_tensor* v) 
   return STAR_OK;
 }
 
+// Partition offsets (host [P + 1]) and the split chunk length per
+// partition: c_j = roundup(ceil(n_j / splits), STAR_SPLIT_ALIGN).
+int check_parts(const int64_t* part_offsets, int32_t P, int32_t splits, int64_t rows,
+                int64_t* chunk) {
+  if (part_offsets == nullptr) return STAR_ERR_NULL;
+  if (P < 1 || P > STAR_MAX_PARTS || splits < 1 || splits > 1024) return STAR_ERR_SHAPE;
+  if (part_offsets[0] < 0 || part_offsets[P] > rows) return STAR_ERR_SHAPE;
+  for (int j = 0; j < P; ++j)
+    if (part_offsets[j + 1] < part_offsets[j]) return STAR_ERR_SHAPE;
+  for (int j = 0; j < P; ++j) {
+    const int64_t n = part_offsets[j + 1] - part_offsets[j];
+    int64_t c = (n + splits - 1) / splits;
+    c = (c + STAR_SPLIT_ALIGN - 1) / STAR_SPLIT_ALIGN * STAR_SPLIT_ALIGN;
+    chunk[j] = c;
+  }
+  return STAR_OK;
+}
+
+// Split-KV decode launch parameters common to the partial and fused paths.
+void decode_params(star::DecodeParams& p, const star_tensor* q, const star_tensor* k_cache,
+                   const star_tensor* v_cache, const int64_t* part_offsets, int32_t P,
+                   int32_t splits, const int64_t* chunk, int64_t q_pos0, float scale,
+                   float* o_part, float* lse_part) {
+  std::memset(&p, 0, sizeof(p));
+  p.q = ref(q);
+  p.k = ref(k_cache);
+  p.v = ref(v_cache);
+  p.B = (int32_t)q->B;
+  p.Hq = (int32_t)q->H;
+  p.Hkv = (int32_t)k_cache->H;
+  p.g = (int32_t)(q->H / k_cache->H);
+  p.D = (int32_t)q->D;
+  p.in_f32 = q->dtype == STAR_F32;
+  p.Lq = q->S;
+  p.kv_rows = k_cache->S;
+  p.q_pos0 = q_pos0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.P = P;
+  p.splits = splits;
+  for (int j = 0; j <= P; ++j) p.offs[j] = part_offsets[j];
+  for (int j = 0; j < P; ++j) p.chunk[j] = chunk[j];
+  p.opart = o_part;
+  p.lse = lse_part;
+}
+
 // Validation shared by the two Phase-1 entry points.
 int check_phase1(const star_tensor* q, const star_tensor* k, const star_tensor* v,
                  int64_t block_b, float scale, const star_tensor* o, const float* lse) {
@@ -315,46 +361,18 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
                         float* lse_part, void* stream) {
   int s;
   if ((s = check_qkv(q, k_cache, v_cache)) != STAR_OK) return s;
-  if (part_offsets == nullptr || o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
-  if (P < 1 || P > STAR_MAX_PARTS || splits < 1 || splits > 1024) return STAR_ERR_SHAPE;
+  if (o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
+  int64_t chunk[STAR_MAX_PARTS];
+  if ((s = check_parts(part_offsets, P, splits, k_cache->S, chunk)) != STAR_OK) return s;
   if (q_pos0 < 0) return STAR_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
-  if (part_offsets[0] < 0 || part_offsets[P] > k_cache->S) return STAR_ERR_SHAPE;
-  for (int j = 0; j < P; ++j)
-    if (part_offsets[j + 1] < part_offsets[j]) return STAR_ERR_SHAPE;
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return STAR_ERR_ALIGN;
   if (q->S == 0) return STAR_OK;
-  int64_t chunk[STAR_MAX_PARTS];
-  for (int j = 0; j < P; ++j) {
-    const int64_t n = part_offsets[j + 1] - part_offsets[j];
-    int64_t c = (n + splits - 1) / splits;
-    c = (c + STAR_SPLIT_ALIGN - 1) / STAR_SPLIT_ALIGN * STAR_SPLIT_ALIGN;
-    chunk[j] = c;
-  }
   const int g = (int)(q->H / k_cache->H);
   if (star::decode_supported(g, q->S, (int)q->D)) {
     star::DecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.q = ref(q);
-    p.k = ref(k_cache);
-    p.v = ref(v_cache);
-    p.B = (int32_t)q->B;
-    p.Hq = (int32_t)q->H;
-    p.Hkv = (int32_t)k_cache->H;
-    p.g = g;
-    p.D = (int32_t)q->D;
-    p.in_f32 = q->dtype == STAR_F32;
-    p.Lq = q->S;
-    p.kv_rows = k_cache->S;
-    p.q_pos0 = q_pos0;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.P = P;
-    p.splits = splits;
-    for (int j = 0; j <= P; ++j) p.offs[j] = part_offsets[j];
-    for (int j = 0; j < P; ++j) p.chunk[j] = chunk[j];
-    p.opart = o_part;
-    p.lse = lse_part;
+    decode_params(p, q, k_cache, v_cache, part_offsets, P, splits, chunk, q_pos0, scale, o_part,
+                  lse_part);
     return hip_status(star::launch_decode(p, (hipStream_t)stream));
   }
   star::FlashParams p;
@@ -384,6 +402,70 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
   p.lse = lse_part;
   p.opart = o_part;
   return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
+                     const star_tensor* v_new, const star_tensor* k_cache,
+                     const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
+                     int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
+                     float scale, float* o_part, float* lse_part, const star_tensor* o,
+                     float* lse, void* stream) {
+  int s;
+  if ((s = check_qkv(q_new, k_cache, v_cache)) != STAR_OK) return s;
+  if ((s = check_tensor(k_new, false)) != STAR_OK) return s;
+  if ((s = check_tensor(v_new, false)) != STAR_OK) return s;
+  if ((s = check_tensor(o, true)) != STAR_OK) return s;
+  if (q_new->dtype != STAR_BF16) return STAR_ERR_DTYPE;
+  if (o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
+  if (q_new->S != 1 || k_new->S != 1 || v_new->S != 1) return STAR_ERR_SHAPE;
+  for (const star_tensor* t : {k_new, v_new})
+    if (t->B != k_cache->B || t->H != k_cache->H || t->D != k_cache->D) return STAR_ERR_SHAPE;
+  if (o->B != q_new->B || o->H != q_new->H || o->S != 1 || o->D != q_new->D) return STAR_ERR_SHAPE;
+  int64_t chunk[STAR_MAX_PARTS];
+  if ((s = check_parts(part_offsets, P, splits, k_cache->S, chunk)) != STAR_OK) return s;
+  if (slot < part_offsets[0] || slot >= part_offsets[P] || pos < 0) return STAR_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
+  if (rope && !(std::isfinite(base) && base > 1.0)) return STAR_ERR_SHAPE;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return STAR_ERR_ALIGN;
+  star::DecodeParams p;
+  decode_params(p, q_new, k_cache, v_cache, part_offsets, P, splits, chunk, pos, scale, o_part,
+                lse_part);
+  p.fused = 1;
+  p.rope = rope != 0;
+  p.kn = ref(k_new);
+  p.vn = ref(v_new);
+  p.slot = slot;
+  if (p.rope) {
+    // the token's angles, exact in fp64, rounded once to fp32
+    double inv_freq[64];
+    fill_inv_freq(inv_freq, q_new->D, base);
+    for (int64_t j = 0; j < q_new->D / 2; ++j) {
+      const double a = (double)pos * inv_freq[j];
+      p.rc[j] = (float)std::cos(a);
+      p.rs[j] = (float)std::sin(a);
+    }
+  }
+  if ((s = hip_status(star::launch_decode(p, (hipStream_t)stream))) != STAR_OK) return s;
+  // the merge runs as the next launch on the same stream: the kernel
+  // boundary makes every workgroup's partial visible to it
+  star::MergeParams m;
+  std::memset(&m, 0, sizeof(m));
+  m.opart = o_part;
+  m.lsep = lse_part;
+  m.N = P * splits;
+  m.R = q_new->B * q_new->H;
+  m.D = (int32_t)q_new->D;
+  m.H = (int32_t)q_new->H;
+  m.S = 1;
+  m.o = o->data;
+  m.o_f32 = o->dtype == STAR_F32;
+  m.osB = o->sB;
+  m.osH = o->sH;
+  m.osS = o->sS;
+  m.lse = lse;
+  return hip_status(star::launch_merge(m, (hipStream_t)stream));
 }
 
 int star_lse_merge(const float* o_part, const float* lse_part, int32_t N, const star_tensor* o,

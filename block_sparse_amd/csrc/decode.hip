@@ -59,7 +59,7 @@ __device__ __forceinline__ int v_chunk_off(int row, int chunk) {
   return row * (D * 2) + (((chunk ^ swz(row)) & (D / 8 - 1)) << 4);
 }
 
-template <int D, typename T>
+template <int D, typename T, bool FUSED>
 __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) {
   constexpr int NDC = D / 32;   // k-steps of 32 along D
   constexpr int NDB = D / 16;   // 16-row blocks of O^T
@@ -107,6 +107,62 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       u32x4 v = {0, 0, 0, 0};
       if (row_ok) v = Load8<T>::load(qr + 32 * dc + 8 * kg);
       qf[dc] = as_bf16x8(v);
+    }
+    if constexpr (FUSED) {
+      // rotate-half RoPE of the raw query row at the new token's position:
+      // the lane holds d = 32 dc + 8 kg + e and its partner d + D/2 in
+      // register dc + NDC/2; the result is rounded to bf16 as stored q is
+      if (p.rope) {
+#pragma unroll
+        for (int dc = 0; dc < NDC / 2; ++dc) {
+          bf16x8 y1, y2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 32 * dc + 8 * kg + e;
+            const float c = p.rc[j], sn = p.rs[j];
+            const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + NDC / 2][e];
+            y1[e] = (__bf16)(x1 * c - x2 * sn);
+            y2[e] = (__bf16)(x2 * c + x1 * sn);
+          }
+          qf[dc] = y1;
+          qf[dc + NDC / 2] = y2;
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // the workgroup whose chunk holds the new token's slot appends its K/V
+    // row (K rotated like q) before any of its waves loads the chunk
+    if (p.slot >= c0 && p.slot < c1) {
+      if (tid < D / 16) {
+        const int ch = tid, half = D / 2;
+        const __bf16* kn = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
+                           (int64_t)kvh * p.kn.sH;
+        const __bf16* vn = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
+                           (int64_t)kvh * p.vn.sH;
+        __bf16* kc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.k.data)) +
+                     (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH + p.slot * p.k.sS;
+        __bf16* vc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.v.data)) +
+                     (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH + p.slot * p.v.sS;
+        const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const u32x4*>(kn + 8 * ch));
+        const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const u32x4*>(kn + half + 8 * ch));
+        bf16x8 y1 = x1, y2 = x2;
+        if (p.rope) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float c = p.rc[8 * ch + e], sn = p.rs[8 * ch + e];
+            const float a1 = (float)x1[e], a2 = (float)x2[e];
+            y1[e] = (__bf16)(a1 * c - a2 * sn);
+            y2[e] = (__bf16)(a2 * c + a1 * sn);
+          }
+        }
+        *reinterpret_cast<bf16x8*>(kc + 8 * ch) = y1;
+        *reinterpret_cast<bf16x8*>(kc + half + 8 * ch) = y2;
+        *reinterpret_cast<u32x4*>(vc + 8 * ch) = *reinterpret_cast<const u32x4*>(vn + 8 * ch);
+        *reinterpret_cast<u32x4*>(vc + half + 8 * ch) =
+            *reinterpret_cast<const u32x4*>(vn + half + 8 * ch);
+      }
+      __syncthreads();   // stores complete and visible to this workgroup's loads
     }
   }
 
@@ -292,12 +348,16 @@ hipError_t launch_decode(DecodeParams& p, hipStream_t stream) {
   if (items > 0x7fffffff) return hipErrorInvalidValue;
   p.total_items = (int32_t)items;
   const dim3 grid(p.total_items), block(NWD * 64);
-  if (p.D == 128) {
-    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<128, float>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<128, __bf16>), grid, block, 0, stream, p);
+  if (p.fused) {
+    if (p.in_f32) return hipErrorInvalidValue;
+    if (p.D == 128) hipLaunchKernelGGL((decode_kernel<128, __bf16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<64, __bf16, true>), grid, block, 0, stream, p);
+  } else if (p.D == 128) {
+    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<128, float, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<128, __bf16, false>), grid, block, 0, stream, p);
   } else {
-    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<64, float>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<64, __bf16>), grid, block, 0, stream, p);
+    if (p.in_f32) hipLaunchKernelGGL((decode_kernel<64, float, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<64, __bf16, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -71,6 +71,14 @@ struct DecodeParams {
   int32_t total_items;
   float* opart;
   float* lse;
+  // fused decode step (star_decode_step, one query row per head): rope of
+  // q and of the new K row (angles' cos/sin precomputed on the host) and
+  // the append of the new K/V row by the workgroup whose chunk holds its slot
+  int32_t fused;
+  int32_t rope;
+  TensorRef kn, vn;        // the new token's K (un-rotated) and V, [B, Hkv, 1, D]
+  int64_t slot;            // cache row the new token is written to
+  float rc[64], rs[64];    // cos / sin of the new token's angle for pair j
 };
 
 bool decode_supported(int g, int64_t Lq, int D);

@@ -12,105 +12,103 @@
 namespace star {
 namespace {
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 constexpr int MW = 8;  // waves per row
 
-// One workgroup per row.  Pass 1: all threads stride the N statistics for
-// the max and the sum of exp (block reductions through LDS).  Pass 2: wave w
-// takes partials w, w + MW, ...; each lane owns D/64 output columns; eight
-// partials' loads are issued before any is used, so a row costs a few
-// memory latencies whatever N is.  The MW waves' sums meet in LDS.
+// One workgroup per row, one pass over the partials.  Wave w takes partials
+// w, w + MW, ... in batches of U (their statistics and output columns are
+// loaded together, so a batch costs one memory latency) and keeps a running
+// (max, sum of exp, weighted output) for them, rescaled when the max grows.
+// The MW waves' running values are then merged the same way through LDS.
+// Every lane of a wave handles the same partials, so the running max and
+// sum are wave-uniform; each lane owns D/64 output columns.
 template <int D>
 __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   constexpr int PER = D / 64;
   constexpr int U = 8;
-  __shared__ float red[MW];
-  __shared__ float part[MW][D];
+  __shared__ float wm[MW], ws[MW];
+  __shared__ float wacc[MW][D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int N = p.N;
   const float* ls = p.lsep + row;
+  const float* ob = p.opart + row * D + lane * PER;
 
-  float m = -INFINITY;
-  for (int n = tid; n < N; n += MW * 64) m = fmaxf(m, ls[(int64_t)n * p.R]);
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = red[0];
-#pragma unroll
-  for (int w = 1; w < MW; ++w) m = fmaxf(m, red[w]);
-  __syncthreads();
-  float lse = -INFINITY;
+  float m = -INFINITY, sum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  if (m != -INFINITY) {
-    float sum = 0.f;
-    for (int n = tid; n < N; n += MW * 64) sum += __expf(ls[(int64_t)n * p.R] - m);
-    sum = wave_sum(sum);
-    if (lane == 0) red[wave] = sum;
-    __syncthreads();
-    sum = 0.f;
+  for (int n0 = wave; n0 < N; n0 += MW * U) {
+    float sn[U];
+    float v[U][PER];
 #pragma unroll
-    for (int w = 0; w < MW; ++w) sum += red[w];
-    lse = m + __logf(sum);
-    const float* ob = p.opart + row * D + lane * PER;
-    for (int n0 = wave; n0 < N; n0 += MW * U) {
-      float wt[U];
-      float v[U][PER];
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * MW;
+      sn[u] = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int n = n0 + u * MW;
-        wt[u] = 0.f;
+      for (int i = 0; i < PER; ++i) v[u][i] = 0.f;
+      if (n < N) {
+        sn[u] = ls[(int64_t)n * p.R];
+        const float* src = ob + (int64_t)n * p.R * D;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) v[u][i] = 0.f;
-        if (n < N) {
-          const float sn = ls[(int64_t)n * p.R];
-          wt[u] = (sn == -INFINITY) ? 0.f : __expf(sn - lse);
-          const float* src = ob + (int64_t)n * p.R * D;
-#pragma unroll
-          for (int i = 0; i < PER; ++i) v[u][i] = src[i];
-        }
+        for (int i = 0; i < PER; ++i) v[u][i] = src[i];
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += wt[u] * v[u][i];
     }
+    float bm = sn[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) bm = fmaxf(bm, sn[u]);
+    if (bm == -INFINITY) continue;            // only empty partials in this batch
+    const float nm = fmaxf(m, bm);
+    const float f = (m == -INFINITY) ? 0.f : __expf(m - nm);
+    sum *= f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] *= f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = (sn[u] == -INFINITY) ? 0.f : __expf(sn[u] - nm);
+      sum += w;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += w * v[u][i];
+    }
+    m = nm;
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    ws[wave] = sum;
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) part[wave][lane * PER + i] = acc[i];
+  for (int i = 0; i < PER; ++i) wacc[wave][lane * PER + i] = acc[i];
   __syncthreads();
   if (wave != 0) return;
+  float M = wm[0];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    float o = 0.f;
+  for (int w = 1; w < MW; ++w) M = fmaxf(M, wm[w]);
+  float S = 0.f;
+  float o[PER];
 #pragma unroll
-    for (int w = 0; w < MW; ++w) o += part[w][lane * PER + i];
-    acc[i] = o;
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < MW; ++w) {
+      const float f = (wm[w] == -INFINITY) ? 0.f : __expf(wm[w] - M);
+      S += f * ws[w];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += f * wacc[w][lane * PER + i];
+    }
   }
+  const float inv = S > 0.f ? 1.0f / S : 0.f;
+  const float lse = S > 0.f ? M + __logf(S) : -INFINITY;
   const int64_t s = row % p.S;
   const int64_t bh = row / p.S;
   const int64_t h = bh % p.H, b = bh / p.H;
   const int64_t off = b * p.osB + h * p.osH + s * p.osS + lane * PER;
   if (p.o_f32) {
-    float* o = reinterpret_cast<float*>(p.o) + off;
+    float* out = reinterpret_cast<float*>(p.o) + off;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = acc[i];
+    for (int i = 0; i < PER; ++i) out[i] = o[i] * inv;
   } else {
-    __bf16* o = reinterpret_cast<__bf16*>(p.o) + off;
+    __bf16* out = reinterpret_cast<__bf16*>(p.o) + off;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = (__bf16)acc[i];
+    for (int i = 0; i < PER; ++i) out[i] = (__bf16)(o[i] * inv);
   }
   if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
 }

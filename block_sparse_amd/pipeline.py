@@ -11,7 +11,8 @@ review "What carries the argument"; atlas.scime.ai summary "Approach"):
   Phase 2  query tokens: rope(q) at L.., append their K/V to the last
            partition (the query host), partials over every partition and
            the LSE merge.  Then each generated token repeats the same with
-           one row, attending to everything cached so far.
+           one row, attending to everything cached so far: rope, append and
+           partials in one launch per token, then the merge.
 
 Phase-1 variants (same cache afterwards, so Phase 2 is unchanged):
   anchor at other position ids  the anchor's un-rotated keys re-rotated per
@@ -30,8 +31,8 @@ import math
 
 import torch
 
-from . import (decode_prepare, gather_rows, kv_append, lse_merge, phase1_blocklocal,
-               phase1_prefix, phase2_partial, pulsar_prefix, rope_apply)
+from . import (decode_prepare, decode_step, gather_rows, kv_append, lse_merge,
+               phase1_blocklocal, phase1_prefix, phase2_partial, pulsar_prefix, rope_apply)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -54,7 +55,7 @@ class StarAttentionStep:
 
     def __init__(self, B, Hq, Hkv, D, L, b, Lq, T, anchor=None, rope=True,
                  base=500000.0, device="cuda", want_lse=True,
-                 splits_query=None, splits_decode=None):
+                 splits_query=None, splits_decode=None, fused_decode=True):
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
         self.L, self.b, self.Lq, self.T = L, b, Lq, T
         self.a = b if anchor is None else anchor
@@ -85,6 +86,8 @@ class StarAttentionStep:
         self.lp_q = torch.empty((nq, B, Hq, max(Lq, 1)), dtype=torch.float32, device=dev)
         self.op_d = torch.empty((nd, B, Hq, 1, D), dtype=torch.float32, device=dev)
         self.lp_d = torch.empty((nd, B, Hq, 1), dtype=torch.float32, device=dev)
+        # rope + append + partials in one launch per token (star_decode_step)
+        self.fused_decode = fused_decode
 
     # -- inputs -----------------------------------------------------------
     def load_context(self, v):
@@ -174,6 +177,12 @@ class StarAttentionStep:
     def decode(self, t, qd, kd, vd):
         """Generated token t (inputs are views [B, H, 1, D])."""
         pos = self.L + self.Lq + t
+        if self.fused_decode:
+            offs = partition_offsets(self.L, self.b, pos + 1)
+            decode_step(qd, kd, vd, self.kc, self.vc, pos, pos, offs, self.sd, self.op_d,
+                        self.lp_d, self.od[:, :, t:t + 1], self.lsed[t],
+                        base=self.base, rope=self.rope, scale=self.scale)
+            return
         qv = self.qd_r[:, :, t:t + 1]
         decode_prepare(qd, qv, kd, vd, self.kc, self.vc, slot0=pos, pos0=pos, base=self.base,
                        rope=self.rope)

@@ -275,6 +275,36 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
 int star_lse_merge(const float* o_part, const float* lse_part, int32_t N,
                    const star_tensor* o, float* lse, void* stream);
 
+/*
+ * One whole decode step of one generated token: the token's query and key
+ * are rotated at `pos` (when rope != 0), its K/V row is appended at cache
+ * row `slot`, and the split-KV partials over every partition are computed
+ * exactly as star_phase2_partial does (Lq = 1, q_pos0 = pos) -- all in one
+ * launch -- followed by the star_lse_merge of those partials.  Each
+ * generated token attends globally to every cached token (Pith review of
+ * Star Attention, "What carries the argument", "Core claim" and
+ * "Circularity Check").  The cos/sin of the token's angles are computed on
+ * the host in fp64 and rounded once to fp32.
+ *
+ *   q_new             [B, Hq, 1, D] bf16, un-rotated.
+ *   k_new, v_new      [B, Hkv, 1, D] bf16 (k un-rotated).
+ *   k_cache, v_cache  [B, Hkv, S, D] bf16; row `slot` is overwritten.
+ *   part_offsets      host int64 [P + 1] as for star_phase2_partial;
+ *                     part_offsets[0] <= slot < part_offsets[P].
+ *   o_part, lse_part  device fp32 workspaces of star_phase2_partial's sizes
+ *                     ([P*splits, B, Hq, 1, D] and [P*splits, B, Hq]);
+ *                     they hold the chunk partials afterwards.
+ *   o                 [B, Hq, 1, D] bf16 or fp32 merged output.
+ *   lse               fp32 [B, Hq] contiguous merged lse, or NULL.
+ */
+int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
+                     const star_tensor* v_new, const star_tensor* k_cache,
+                     const star_tensor* v_cache, int64_t slot, int64_t pos,
+                     double base, int32_t rope, const int64_t* part_offsets,
+                     int32_t P, int32_t splits, float scale, float* o_part,
+                     float* lse_part, const star_tensor* o, float* lse,
+                     void* stream);
+
 /* Human-readable name of a star_status value (static storage). */
 const char* star_status_string(int status);
 

@@ -225,3 +225,31 @@ def test_pulsar_prefix_host_validation(lib):
     assert P(cap=0) == -2 and n.value > 0            # too small: reports the size
     rows = (ctypes.c_int64 * n.value)()
     assert P(rows=rows, cap=n.value) == 0
+
+
+def test_decode_step_validation(lib):
+    qn = T(B=1, H=8, S=1, D=128)
+    kn, vn = T(B=1, H=2, S=1, D=128), T(B=1, H=2, S=1, D=128)
+    kc, vc = T(B=1, H=2, S=100, D=128), T(B=1, H=2, S=100, D=128)
+    o = T(B=1, H=8, S=1, D=128, dtype=1)
+
+    def ds(q=qn, k=kn, oo=o, slot=50, pos=50, offs=(0, 40, 51), splits=2, op=FAKE, lp=FAKE,
+           base=5e5, rope=1):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        return lib.star_decode_step(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vn),
+                                    ctypes.byref(kc), ctypes.byref(vc), slot, pos, base, rope,
+                                    arr, len(offs) - 1, splits, 0.1, op, lp, ctypes.byref(oo),
+                                    None, None)
+    assert ds(slot=51) == -2                       # slot outside the partitions
+    assert ds(slot=-1) == -2
+    assert ds(pos=-1) == -2
+    assert ds(q=T(B=1, H=8, S=2, D=128)) == -2     # one token per call
+    assert ds(k=T(B=1, H=2, S=1, D=64)) == -2
+    assert ds(oo=T(B=1, H=8, S=2, D=128)) == -2
+    assert ds(q=T(B=1, H=8, S=1, D=128, dtype=1)) == -3
+    assert ds(op=None) == -1
+    assert ds(op=FAKE + 4) == -4
+    assert ds(offs=(0, 60, 51)) == -2
+    assert ds(offs=(0, 40, 101)) == -2
+    assert ds(base=1.0) == -2
+    assert ds(splits=0) == -2

@@ -194,3 +194,66 @@ def test_decode_prepare_parity(rope):
         assert (np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-5).all()
     assert np.array_equal(host64(vc)[:, :, 40:43], f64(vn))
     assert (host64(kc)[:, :, :40] == 0).all() and (host64(kc)[:, :, 43:] == 0).all()
+
+
+DSTEP_CASES = [
+    # B, Hq, Hkv, D, L, b, splits, rope, T
+    (2, 8, 2, 128, 777, 200, 4, True, 5),
+    (1, 16, 1, 64, 300, 100, 8, False, 3),      # g = 16, D = 64, empty chunks
+    (1, 32, 8, 128, 2000, 512, 3, True, 4),
+    (1, 4, 4, 128, 70, 64, 1, True, 2),         # MHA, short context
+]
+
+
+@pytest.mark.parametrize("case", DSTEP_CASES, ids=[str(i) for i in range(len(DSTEP_CASES))])
+def test_decode_step_parity(case):
+    """The fused decode step (rope, append and partials in one launch, then
+    the merge) against the oracle's global attention and cache over several
+    consecutive tokens, and against the unfused call sequence."""
+    from block_sparse_amd.pipeline import StarAttentionStep
+    B, Hq, Hkv, D, L, b, splits, rope, T = case
+    print(f"decode_step case {case}", flush=True)
+    g = Hq // Hkv
+    base = 500000.0
+    q = rand_tensor(51, 0, B, Hq, L, D)
+    k = rand_tensor(51, 1, B, Hkv, L, D)
+    v = rand_tensor(51, 2, B, Hkv, L, D)
+    qd = rand_tensor(51, 6, B, Hq, T, D)
+    kd = rand_tensor(51, 7, B, Hkv, T, D)
+    vd = rand_tensor(51, 8, B, Hkv, T, D)
+    outs = []
+    for fused in (True, False):
+        st = StarAttentionStep(B, Hq, Hkv, D, L, b, 0, T, rope=rope, base=base,
+                               splits_decode=splits, fused_decode=fused)
+        st.load_context(to_dev(v))
+        st.rope_context(to_dev(q), to_dev(k))
+        dq, dk, dv = to_dev(qd), to_dev(kd), to_dev(vd)
+        for t in range(T):
+            st.decode(t, dq[:, :, t:t + 1], dk[:, :, t:t + 1], dv[:, :, t:t + 1])
+        torch.cuda.synchronize()
+        outs.append((host64(st.od), host64(st.lsed), host64(st.kc), host64(st.vc)))
+    (o_f, l_f, kc_f, vc_f), (o_u, l_u, kc_u, vc_u) = outs
+    pos_c = np.arange(L)
+    pos_d = L + np.arange(T)
+    rot = (lambda x, p: so.round_bf16(so.rope(x, p, base))) if rope else (lambda x, p: x)
+    K = np.concatenate([rot(f64(k), pos_c), rot(f64(kd), pos_d)], axis=2)
+    V = np.concatenate([f64(v), f64(vd)], axis=2)
+    # the appended rows: rotated k (bf16 rounding of the exact rotation) and v
+    got_k = kc_f[:, :, L:L + T]
+    assert (np.abs(got_k - K[:, :, L:]) <= np.abs(K[:, :, L:]) * 2.0**-8 + 1e-5).all()
+    assert np.array_equal(vc_f[:, :, L:L + T], f64(vd))
+    Qd = rot(f64(qd), pos_d)
+    ref_o = np.zeros((B, Hq, T, D))
+    ref_l = np.zeros((T, B, Hq))
+    for t in range(T):
+        parts = so.partitions(L, b, L + t + 1)
+        for bb in range(B):
+            for h in range(Hq):
+                o, l, _, _ = so.phase2(Qd[bb, h, t:t + 1], pos_d[t:t + 1], K[bb, h // g],
+                                       V[bb, h // g], parts, 1 / math.sqrt(D))
+                ref_o[bb, h, t], ref_l[t, bb, h] = o[0], l[0]
+    check_out(o_f[:, :, :T], ref_o, "fused O")
+    check_lse(l_f[:T], ref_l, "fused LSE")
+    check_out(o_u[:, :, :T], ref_o, "unfused O")
+    assert np.abs(o_f[:, :, :T] - o_u[:, :, :T]).max() < 2e-3
+    assert np.abs(l_f[:T] - l_u[:T]).max() < 2e-4
