@@ -97,39 +97,6 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const int64_t qpos = p.q_pos0 + qi;
   const int64_t min_qpos = p.q_pos0;   // rows are ordered by query index
 
-  // Q^T as the B operand: lane (row n, group kg) holds d = 32dc + 8kg + e.
-  bf16x8 qf[NDC];
-  {
-    const T* qr = reinterpret_cast<const T*>(p.q.data) + (int64_t)b * p.q.sB +
-                  (int64_t)(row_ok ? head : 0) * p.q.sH + (int64_t)(row_ok ? qi : 0) * p.q.sS;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      u32x4 v = {0, 0, 0, 0};
-      if (row_ok) v = Load8<T>::load(qr + 32 * dc + 8 * kg);
-      qf[dc] = as_bf16x8(v);
-    }
-    if constexpr (FUSED) {
-      // rotate-half RoPE of the raw query row at the new token's position:
-      // the lane holds d = 32 dc + 8 kg + e and its partner d + D/2 in
-      // register dc + NDC/2; the result is rounded to bf16 as stored q is
-      if (p.rope) {
-#pragma unroll
-        for (int dc = 0; dc < NDC / 2; ++dc) {
-          bf16x8 y1, y2;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 32 * dc + 8 * kg + e;
-            const float c = p.rc[j], sn = p.rs[j];
-            const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + NDC / 2][e];
-            y1[e] = (__bf16)(x1 * c - x2 * sn);
-            y2[e] = (__bf16)(x2 * c + x1 * sn);
-          }
-          qf[dc] = y1;
-          qf[dc + NDC / 2] = y2;
-        }
-      }
-    }
-  }
   if constexpr (FUSED) {
     // the workgroup whose chunk holds the new token's slot appends its K/V
     // row (K rotated like q) before any of its waves loads the chunk
@@ -168,12 +135,6 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
 
   const T* kbase = reinterpret_cast<const T*>(p.k.data) + (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH;
   const T* vbase = reinterpret_cast<const T*>(p.v.data) + (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH;
-
-  f32x4 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2 = -INFINITY, lsum = 0.f;
-  const float c2 = p.scale_log2;
 
   const int nt = (int)((c1 - c0 + KTD - 1) / KTD);
   uint8_t* vs = smem + wave * VT;
@@ -218,6 +179,50 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       }
     }
   };
+
+  // the first two tiles go out before the query is loaded and rotated
+  // this wave's tiles: wave, wave + NWD, ...; two in flight at any time
+  if (wave < nt) load_tile(0, wave);
+  if (wave + NWD < nt) load_tile(1, wave + NWD);
+
+  // Q^T as the B operand: lane (row n, group kg) holds d = 32dc + 8kg + e.
+  bf16x8 qf[NDC];
+  {
+    const T* qr = reinterpret_cast<const T*>(p.q.data) + (int64_t)b * p.q.sB +
+                  (int64_t)(row_ok ? head : 0) * p.q.sH + (int64_t)(row_ok ? qi : 0) * p.q.sS;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      u32x4 v = {0, 0, 0, 0};
+      if (row_ok) v = Load8<T>::load(qr + 32 * dc + 8 * kg);
+      qf[dc] = as_bf16x8(v);
+    }
+    if constexpr (FUSED) {
+      // rotate-half RoPE of the raw query row at the new token's position:
+      // the lane holds d = 32 dc + 8 kg + e and its partner d + D/2 in
+      // register dc + NDC/2; the result is rounded to bf16 as stored q is
+      if (p.rope) {
+#pragma unroll
+        for (int dc = 0; dc < NDC / 2; ++dc) {
+          bf16x8 y1, y2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 32 * dc + 8 * kg + e;
+            const float c = p.rc[j], sn = p.rs[j];
+            const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + NDC / 2][e];
+            y1[e] = (__bf16)(x1 * c - x2 * sn);
+            y2[e] = (__bf16)(x2 * c + x1 * sn);
+          }
+          qf[dc] = y1;
+          qf[dc + NDC / 2] = y2;
+        }
+      }
+    }
+  }
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY, lsum = 0.f;
+  const float c2 = p.scale_log2;
 
   // one tile held in staging slot SL; the slot is refilled with the tile
   // two steps ahead right after its registers are consumed
@@ -290,9 +295,6 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
     asm volatile("" ::: "memory");
   };
 
-  // this wave's tiles: wave, wave + NWD, ...; two in flight at any time
-  if (wave < nt) load_tile(0, wave);
-  if (wave + NWD < nt) load_tile(1, wave + NWD);
   for (int t = wave; t < nt; t += 2 * NWD) {
     process(std::integral_constant<int, 0>{}, t);
     if (t + NWD >= nt) break;
