@@ -168,6 +168,56 @@ def phase1_variants(st, dev, w, x, ev, reps=3):
     return out
 
 
+def phase1_layer(w, ev, reps=3):
+    """One Llama-3 attention layer around Phase 1 on the same shapes (seeded
+    input stream and random weights): RMSNorm, the fused q/k/v projection
+    (rocBLAS), RoPE, Phase 1 and the output projection with the residual,
+    timed per stage with HIP events after one warm-up pass."""
+    import numpy as np
+    import torch
+
+    from block_sparse_amd.layer import AttentionLayers
+    from workloads import RMS_EPS, layer_inputs
+    inp = layer_inputs(w, 1)
+    todev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    layers = [{k: todev(v) for k, v in inp["layers"][0].items()}]
+    x = todev(inp["x"])
+    del inp
+    st = AttentionLayers(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, layers, anchor=w.a, rope=w.rope,
+                         base=w.base, eps=RMS_EPS)
+    st.forward(x)
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(reps):
+        marks = [("start", ev())]
+        marks[0][1].record()
+        def mark(name):
+            e = ev()
+            e.record()
+            marks.append((name, e))
+        st.forward(x, mark)
+        runs.append(marks)
+    torch.cuda.synchronize()
+    stages = {}
+    for marks in runs:
+        for (_, e0), (name, e1) in zip(marks, marks[1:]):
+            stages.setdefault(name, []).append(e0.elapsed_time(e1))
+    st_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    total = sum(st_ms.values())
+    gf = st.gemm_flops()
+    af = phase1_flops(w)
+    gemm_ms = st_ms["qkv_proj"] + st_ms["o_proj"]
+    out = {"ms": total, "stages_ms": st_ms,
+           "context_tokens_per_s": w.B * w.L / (total * 1e-3),
+           "gemm_tflops": gf / (gemm_ms * 1e-3) / 1e12,
+           "phase1_tflops": af / (st_ms["phase1"] * 1e-3) / 1e12,
+           "layer_tflops": (gf + af) / (total * 1e-3) / 1e12,
+           "gemm_flops": gf, "note": "projections in rocBLAS (bf16, fp32 accumulate)"}
+    del st, x, layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_cold(st, dev, w, ev, samples=16):
     """Decode steps timed one at a time, each after a 1 GiB device read that
     evicts the L2 caches and the 256 MiB Infinity Cache, so every K/V byte
@@ -211,6 +261,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache decode timing")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the attention-layer timing (projections + Phase 1)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the Phase-1 prefix variants (Pulsar, anchor positions)")
     ap.add_argument("--splits-decode", type=int, default=None,
@@ -320,6 +372,8 @@ def main():
         out["decode_cold"] = decode_cold(st, dev, w, ev)
     if w.rope and not args.no_variants:
         out["phase1_variants"] = phase1_variants(st, dev, w, x, ev)
+    if not args.no_layer:
+        out["phase1_layer"] = phase1_layer(w, ev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)

@@ -23,7 +23,7 @@ from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
 __all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_prefix",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
-           "split_ranges",
+           "Context", "rmsnorm", "linear", "split_ranges",
            "StarError", "library"]
 
 
@@ -283,3 +283,67 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, slot: int, pos: int, part
                                     ctypes.byref(do), _ptr(lse), _stream(q_new))
     _lib.check("star_decode_step", st)
     return out, lse
+
+
+class Context:
+    """Owner of the library's rocBLAS handle (star_context); needed by
+    :func:`linear`.  Create once and reuse; ``close()`` releases it."""
+
+    def __init__(self):
+        self._ptr = ctypes.c_void_p()
+        _lib.check("star_context_create", library().star_context_create(ctypes.byref(self._ptr)))
+
+    @property
+    def handle(self):
+        return self._ptr
+
+    def close(self):
+        if self._ptr:
+            library().star_context_destroy(self._ptr)
+            self._ptr = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+
+def _mat(t: torch.Tensor) -> _lib.StarTensor:
+    """[M, K] bf16 matrix (unit column stride) as a [1, 1, M, K] descriptor."""
+    if t.dim() != 2:
+        raise ValueError(f"expected a matrix, got shape {tuple(t.shape)}")
+    if t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise TypeError("matrices are bf16 device tensors")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("matrix rows must be contiguous")
+    M, K = t.shape
+    return _lib.StarTensor(t.data_ptr(), _lib.STAR_BF16, 0, 1, 1, M, K, M * t.stride(0),
+                           M * t.stride(0), t.stride(0))
+
+
+def rmsnorm(x, gamma, eps: float = 1e-5, out=None):
+    """Row RMSNorm of ``x`` ([B, H, S, D] or a [M, D] matrix) by ``gamma[D]``."""
+    out = torch.empty_like(x) if out is None else out
+    if gamma.dtype != torch.bfloat16 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bf16 vector")
+    a = _desc(x) if x.dim() == 4 else _mat(x)
+    b = _desc(out) if out.dim() == 4 else _mat(out)
+    st = library().star_rmsnorm(ctypes.byref(a), _ptr(gamma), float(eps), ctypes.byref(b),
+                                _stream(x))
+    _lib.check("star_rmsnorm", st)
+    return out
+
+
+def linear(ctx: Context, x, w, residual=None, out=None):
+    """``out[M, N] = x[M, K] w[N, K]^T (+ residual)`` in rocBLAS (bf16, fp32
+    accumulation)."""
+    if out is None:
+        out = torch.empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16, device=x.device)
+    dx, dw, dy = _mat(x), _mat(w), _mat(out)
+    dr = None if residual is None else _mat(residual)
+    st = library().star_linear(ctx.handle, ctypes.byref(dx), ctypes.byref(dw),
+                               None if dr is None else ctypes.byref(dr), ctypes.byref(dy),
+                               _stream(x))
+    _lib.check("star_linear", st)
+    return out

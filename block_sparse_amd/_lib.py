@@ -19,14 +19,16 @@ STAR_SPLIT_ALIGN = 64
 
 STATUS = {
     0: "STAR_OK", -1: "STAR_ERR_NULL", -2: "STAR_ERR_SHAPE", -3: "STAR_ERR_DTYPE",
-    -4: "STAR_ERR_ALIGN", -5: "STAR_ERR_UNSUPPORTED", -6: "STAR_ERR_HIP",
+    -4: "STAR_ERR_ALIGN", -5: "STAR_ERR_UNSUPPORTED", -6: "STAR_ERR_HIP", -7: "STAR_ERR_BLAS",
 }
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # every symbol include/star_attn.h declares
 EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase1_prefix", "star_gather_rows", "star_pulsar_prefix",
-           "star_phase2_partial", "star_lse_merge", "star_decode_step", "star_status_string",
+           "star_phase2_partial", "star_lse_merge", "star_decode_step",
+           "star_context_create", "star_context_destroy", "star_rmsnorm", "star_linear",
+           "star_status_string",
            "star_abi_version")
 
 
@@ -61,6 +63,10 @@ _SIGS = {
     "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _T, _vp, _vp]),
     "star_decode_step": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _P(_i64), _i32,
                                         _i32, _f32, _vp, _vp, _T, _vp, _vp]),
+    "star_context_create": (ctypes.c_int, [_P(_vp)]),
+    "star_context_destroy": (ctypes.c_int, [_vp]),
+    "star_rmsnorm": (ctypes.c_int, [_T, _vp, _f32, _T, _vp]),
+    "star_linear": (ctypes.c_int, [_vp, _T, _T, _T, _T, _vp]),
     "star_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "star_abi_version": (ctypes.c_int, []),
 }

@@ -1,8 +1,9 @@
 """Build ``libstarattn.so`` (the C-ABI library with the gfx950 kernels).
 
 Every source under ``csrc/`` is compiled by hipcc for gfx950 and linked
-into one shared library next to this file.  The library depends only on
-the HIP runtime; the Python binding loads it with ctypes.
+into one shared library next to this file.  The library depends on the
+HIP runtime and on rocBLAS (for the plain projection GEMMs of the attention
+layer); the Python binding loads it with ctypes.
 
     python -m block_sparse_amd.build
 """
@@ -63,7 +64,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
+           "-lrocblas"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -161,6 +161,7 @@ const char* star_status_string(int status) {
     case STAR_ERR_ALIGN: return "STAR_ERR_ALIGN: data or stride not 16-byte aligned";
     case STAR_ERR_UNSUPPORTED: return "STAR_ERR_UNSUPPORTED: valid request this build does not serve";
     case STAR_ERR_HIP: return "STAR_ERR_HIP: the HIP runtime reported a launch error";
+    case STAR_ERR_BLAS: return "STAR_ERR_BLAS: the BLAS library reported an error";
     default: return "unknown star_status";
   }
 }
@@ -466,6 +467,32 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
   m.osS = o->sS;
   m.lse = lse;
   return hip_status(star::launch_merge(m, (hipStream_t)stream));
+}
+
+int star_rmsnorm(const star_tensor* x, const void* gamma, float eps, const star_tensor* y,
+                 void* stream) {
+  int s;
+  if ((s = check_tensor(x, false)) != STAR_OK) return s;
+  if ((s = check_tensor(y, false)) != STAR_OK) return s;
+  if (gamma == nullptr) return STAR_ERR_NULL;
+  if (!aligned16(gamma)) return STAR_ERR_ALIGN;
+  if (y->B != x->B || y->H != x->H || y->S != x->S || y->D != x->D) return STAR_ERR_SHAPE;
+  if (x->D % 8 != 0 || x->D > 65536) return STAR_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.f) return STAR_ERR_SHAPE;
+  star::RmsParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = ref(x);
+  p.y = y->data;
+  p.ysB = y->sB;
+  p.ysH = y->sH;
+  p.ysS = y->sS;
+  p.gamma = gamma;
+  p.rows = x->B * x->H * x->S;
+  p.S = x->S;
+  p.H = (int32_t)x->H;
+  p.D = (int32_t)x->D;
+  p.eps = eps;
+  return hip_status(star::launch_rmsnorm(p, (hipStream_t)stream));
 }
 
 int star_lse_merge(const float* o_part, const float* lse_part, int32_t N, const star_tensor* o,

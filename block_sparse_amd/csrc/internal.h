@@ -150,4 +150,17 @@ struct GatherParams {
 
 hipError_t launch_gather(GatherParams& p, hipStream_t stream);
 
+// RMSNorm of every row (length D) of a [B, H, S, D] bf16 tensor
+struct RmsParams {
+  TensorRef x;
+  void* y;
+  int64_t ysB, ysH, ysS;
+  const void* gamma;     // bf16 [D]
+  int64_t rows, S;
+  int32_t H, D;
+  float eps;
+};
+
+hipError_t launch_rmsnorm(RmsParams& p, hipStream_t stream);
+
 }  // namespace star

@@ -1,0 +1,58 @@
+// RMSNorm of the residual stream in front of the q/k/v projections (the
+// Llama-3 attention block of the Star Attention pages' HuggingFace models:
+// graphcanon record of NVIDIA/Star-Attention, README).  One wave per row:
+// the sum of squares in fp32, one rounding of x * rsqrt(mean + eps) * gamma
+// to bf16.  HBM-bound: a row is read twice (the second time from cache) and
+// written once.
+#include "common.h"
+#include "internal.h"
+
+namespace star {
+namespace {
+
+constexpr int RW = 4;   // rows (waves) per workgroup
+
+__global__ __launch_bounds__(RW * 64) void rmsnorm_kernel(const RmsParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * RW + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const int64_t s = row % p.S;
+  const int64_t bh = row / p.S;
+  const int64_t h = bh % p.H, b = bh / p.H;
+  const __bf16* x = reinterpret_cast<const __bf16*>(p.x.data) + b * p.x.sB + h * p.x.sH + s * p.x.sS;
+  __bf16* y = reinterpret_cast<__bf16*>(p.y) + b * p.ysB + h * p.ysH + s * p.ysS;
+  const int nch = p.D / 8;
+  float ss = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const bf16x8 v = as_bf16x8(*reinterpret_cast<const u32x4*>(x + 8 * c));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = (float)v[e];
+      ss = __builtin_fmaf(f, f, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  const float r = 1.0f / sqrtf(ss / (float)p.D + p.eps);
+  const __bf16* g = reinterpret_cast<const __bf16*>(p.gamma);
+  for (int c = lane; c < nch; c += 64) {
+    const bf16x8 v = as_bf16x8(*reinterpret_cast<const u32x4*>(x + 8 * c));
+    const bf16x8 gv = as_bf16x8(*reinterpret_cast<const u32x4*>(g + 8 * c));
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)((float)v[e] * r * (float)gv[e]);
+    *reinterpret_cast<bf16x8*>(y + 8 * c) = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(RmsParams& p, hipStream_t stream) {
+  if (p.rows <= 0) return hipSuccess;
+  const int64_t grid = (p.rows + RW - 1) / RW;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)grid), dim3(RW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace star

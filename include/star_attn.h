@@ -58,7 +58,8 @@ typedef enum {
   STAR_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination */
   STAR_ERR_ALIGN = -4,       /* data or stride not 16-byte aligned */
   STAR_ERR_UNSUPPORTED = -5, /* valid request this build does not serve */
-  STAR_ERR_HIP = -6          /* the HIP runtime reported a launch error */
+  STAR_ERR_HIP = -6,         /* the HIP runtime reported a launch error */
+  STAR_ERR_BLAS = -7         /* the BLAS library (rocBLAS) reported an error */
 } star_status;
 
 typedef enum { STAR_BF16 = 0, STAR_F32 = 1 } star_dtype;
@@ -304,6 +305,47 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
                      int32_t P, int32_t splits, float scale, float* o_part,
                      float* lse_part, const star_tensor* o, float* lse,
                      void* stream);
+
+/*
+ * The attention layer around Phase 1 (the Llama-3 attention block of the
+ * pages' HuggingFace models: graphcanon record of NVIDIA/Star-Attention,
+ * README): out = x + Attn(rope(RMSNorm(x) W^T)) Wo^T.  Phase 1 of a
+ * multi-layer model is this layer applied to all L tokens at every layer:
+ * the anchor is causal and first in every augmented block, so its hidden
+ * states, and its K/V, equal block 1's at every layer (Pith review of Star
+ * Attention, "What carries the argument").
+ *
+ * The projections are plain GEMMs and run in rocBLAS; a star_context owns
+ * the rocBLAS handle.  Create one per thread that issues star_linear calls
+ * (star_context_create allocates; it is not a hot call) and destroy it when
+ * done.  Calls with one context must not run concurrently from two threads.
+ */
+typedef struct star_context star_context;
+
+int star_context_create(star_context** ctx);
+int star_context_destroy(star_context* ctx);   /* NULL is a no-op */
+
+/*
+ * RMSNorm of every row: y = x / sqrt(mean(x^2) + eps) * gamma, the sum of
+ * squares in fp32, one rounding to bf16.
+ *   x, y   [B, H, S, D] bf16 (rows of length D, D % 8 == 0); y may alias x
+ *          exactly.
+ *   gamma  device bf16 [D], 16-byte aligned.
+ */
+int star_rmsnorm(const star_tensor* x, const void* gamma, float eps,
+                 const star_tensor* y, void* stream);
+
+/*
+ * y = x w^T (+ residual): bf16 operands, fp32 accumulation, bf16 result.
+ *   x         [1, 1, M, K] (row stride x->sS >= K).
+ *   w         [1, 1, N, K] (the [out, in] weight layout).
+ *   residual  [1, 1, M, N] or NULL; may be y itself.
+ *   y         [1, 1, M, N].
+ * Every row stride times 2 bytes is a multiple of 16.  Returns
+ * STAR_ERR_BLAS if rocBLAS fails.
+ */
+int star_linear(star_context* ctx, const star_tensor* x, const star_tensor* w,
+                const star_tensor* residual, const star_tensor* y, void* stream);
 
 /* Human-readable name of a star_status value (static storage). */
 const char* star_status_string(int status);

@@ -9,4 +9,6 @@ from .star_oracle import (  # noqa: F401
     partial, partitions, phase1, phase1_block_keys, phase1_prefix, phase1_prefix_keys,
     phase1_prefix_rows, phase1_rows, phase2, pulsar_host_length, pulsar_prefix,
     remapped_anchor, rope, rope_theta, round_bf16, star_attention,
+    rmsnorm, layer_projections, layer_output, attention_layer_phase1, causal_layer,
+    star_context_per_host, star_context_layers,
 )

@@ -42,7 +42,10 @@ Readings where the pages leave a step open (all listed in the design notes):
     every block row sees every prefix key;
   * Pulsar: host 0 is plain causal; block 0's chunks that overlap the sink
     are not summary candidates; equal Max-IDF scores go to the earlier chunk;
-    the last chunk of a block may be shorter than m.
+    the last chunk of a block may be shorter than m;
+  * the attention layer is the Llama-3 block: RMSNorm (eps 1e-5), q/k/v
+    projections, RoPE, attention, output projection and the residual add;
+    every stored activation is bf16 (one rounding per stored tensor).
 """
 from __future__ import annotations
 
@@ -512,3 +515,117 @@ def pulsar_host_length(L: int, b: int, sink: int, s: int, i: int) -> int:
     and Eq. 4 as restated there)."""
     n_i = min(b, L - i * b)
     return n_i if i == 0 else n_i + sink + i * s
+
+
+# ----------------------------------------------------------------------------
+# The attention layer around Phase 1 (Llama-3 attention block, any weights)
+# ----------------------------------------------------------------------------
+def rmsnorm(x, gamma, eps: float):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * gamma (the
+    Llama-3 input normalisation; [SA-repo] README: HuggingFace Llama
+    models)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def _maybe_bf16(t, store_bf16: bool):
+    return round_bf16(t) if store_bf16 else t
+
+
+def layer_projections(xs, w, Hq: int, Hkv: int, D: int, eps: float, store_bf16: bool = True):
+    """h = rmsnorm(x); q, k, v = h Wq^T, h Wk^T, h Wv^T for xs [B, n, H].
+    Returns q [B, Hq, n, D], k and v [B, Hkv, n, D] (un-rotated).  Every
+    stored tensor is bf16 in the model, so with ``store_bf16`` h and the
+    projections are rounded to bf16."""
+    B, n, _ = xs.shape
+    h = _maybe_bf16(rmsnorm(xs, w["gamma"], eps), store_bf16)
+    def proj(W, H):
+        y = _maybe_bf16(h @ np.asarray(W, np.float64).T, store_bf16)
+        return y.reshape(B, n, H, D).transpose(0, 2, 1, 3)
+    return proj(w["wq"], Hq), proj(w["wk"], Hkv), proj(w["wv"], Hkv)
+
+
+def layer_output(xs, O, w, store_bf16: bool = True):
+    """out = x + O_flat Wo^T: the output projection and the residual add.
+    O [B, Hq, n, D] is the attention output (stored in bf16)."""
+    B, Hq, n, D = O.shape
+    of = np.asarray(O, np.float64).transpose(0, 2, 1, 3).reshape(B, n, Hq * D)
+    return _maybe_bf16(np.asarray(xs, np.float64) + of @ np.asarray(w["wo"], np.float64).T,
+                       store_bf16)
+
+
+def attention_layer_phase1(x, w, Hq: int, Hkv: int, D: int, b: int, a: int, base: float,
+                           eps: float, rope_on: bool = True, store_bf16: bool = True,
+                           round_output: bool = True):
+    """One attention layer over the whole context with Phase-1 attention, as
+    one device computes it: every token's q/k/v once, the anchor's K/V read
+    from block 1's rows ([SA-pith] "What carries the argument").
+
+    x [B, L, H] (H = Hq*D); w: gamma [H], wq [Hq*D, H], wk/wv [Hkv*D, H],
+    wo [H, Hq*D].  Returns (out [B, L, H], K [B, Hkv, L, D] rotated,
+    V [B, Hkv, L, D]).  ``round_output=False`` leaves the final output in
+    float64 (the intermediate stored tensors are still rounded).
+    """
+    B, L, _ = x.shape
+    q, k, v = layer_projections(x, w, Hq, Hkv, D, eps, store_bf16)
+    pos = np.arange(L)
+    if rope_on:
+        q = _maybe_bf16(rope(q, pos, base), store_bf16)
+        k = _maybe_bf16(rope(k, pos, base), store_bf16)
+    O, _ = phase1(q, k, v, b, a if b < L else 0, 1.0 / math.sqrt(D))
+    O = _maybe_bf16(O, store_bf16)
+    return layer_output(x, O, w, store_bf16 and round_output), k, v
+
+
+def causal_layer(xs, pos, w, Hq: int, Hkv: int, D: int, base: float, eps: float,
+                 rope_on: bool = True, store_bf16: bool = True):
+    """One attention layer with plain causal attention over the sequence xs
+    [B, n, H] whose tokens sit at positions ``pos[n]`` (sequence order is
+    causal order)."""
+    B, n, _ = xs.shape
+    q, k, v = layer_projections(xs, w, Hq, Hkv, D, eps, store_bf16)
+    if rope_on:
+        q = _maybe_bf16(rope(q, pos, base), store_bf16)
+        k = _maybe_bf16(rope(k, pos, base), store_bf16)
+    g = Hq // Hkv
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    O = np.zeros_like(q)
+    for bb in range(B):
+        for h in range(Hq):
+            O[bb, h], _ = attend(q[bb, h], k[bb, h // g], v[bb, h // g], mask, 1.0 / math.sqrt(D))
+    return layer_output(xs, _maybe_bf16(O, store_bf16), w, store_bf16)
+
+
+def star_context_per_host(x, layers, Hq: int, Hkv: int, D: int, b: int, a: int, base: float,
+                          eps: float, rope_on: bool = True, store_bf16: bool = True):
+    """Phase-1 context encoding through a stack of layers exactly as the
+    pages describe it, host by host ([SA-pith] "What carries the argument",
+    [SA-atlas] "Approach"): host 1 runs block 1 through every layer with
+    causal attention; host i >= 2 runs [anchor ; block i] (the anchor = the
+    first a tokens at their original positions) through every layer with
+    causal attention over that augmented sequence and keeps only block i's
+    rows.  Returns the final hidden states [B, L, H]."""
+    B, L, H = x.shape
+    out = np.zeros((B, L, H))
+    for i, (s, e) in enumerate(blocks(L, b)):
+        if i == 0 or a == 0:
+            idx = np.arange(s, e)
+        else:
+            idx = np.concatenate([np.arange(min(a, L)), np.arange(s, e)])
+        xs = np.asarray(x, np.float64)[:, idx]
+        for w in layers:
+            xs = causal_layer(xs, idx, w, Hq, Hkv, D, base, eps, rope_on, store_bf16)
+        out[:, s:e] = xs[:, idx.size - (e - s):]
+    return out
+
+
+def star_context_layers(x, layers, Hq: int, Hkv: int, D: int, b: int, a: int, base: float,
+                        eps: float, rope_on: bool = True, store_bf16: bool = True):
+    """The same stack computed as one device does: every layer applies
+    :func:`attention_layer_phase1` to all L tokens, so the anchor's K/V at
+    every layer are block 1's own rows of that layer."""
+    xs = np.asarray(x, np.float64)
+    for w in layers:
+        xs, _, _ = attention_layer_phase1(xs, w, Hq, Hkv, D, b, a, base, eps, rope_on, store_bf16)
+    return xs

@@ -42,6 +42,8 @@ T_QQ, T_KQ, T_VQ = 3, 4, 5         # query tokens (Phase 2)
 T_QD, T_KD, T_VD = 6, 7, 8         # decode tokens (Phase 2, one per step)
 T_TOK = 9                          # context token ids (Pulsar chunk scoring)
 T_APOS = 10                        # anchor position ids (position-id ablation)
+T_X, T_WQ, T_WK, T_WV, T_WO, T_G = 11, 12, 13, 14, 15, 16   # attention layer
+RMS_EPS = 1e-5                     # Llama-3 RMSNorm epsilon
 
 VOCAB = 128256                     # Llama-3 vocabulary size
 ZIPF_S = 1.1                       # exponent of the token-rank distribution
@@ -249,3 +251,27 @@ def anchor_positions(seed: int, L: int, b: int, a: int) -> list:
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, T_APOS, i])))
         out.append(np.sort(rng.choice(i * b, size=a, replace=False)).astype(np.int64))
     return out
+
+
+# ----------------------------------------------------------------------------
+# inputs of the attention layer around Phase 1 (random weights)
+# ----------------------------------------------------------------------------
+def layer_inputs(w: Workload, n_layers: int = 1, as_bf16: bool = True) -> dict:
+    """Residual-stream input x [B, L, H] (H = Hq*D, N(0,1)) and, per layer,
+    RMSNorm gain gamma [H] (1 + N(0, 0.1^2)) and projection weights in the
+    [out, in] layout: wq [Hq*D, H], wk and wv [Hkv*D, H], wo [H, Hq*D], each
+    N(0, 1/H) so that projections keep unit scale.  Layer i's weights are
+    draws with batch index i.  bf16 bit patterns when ``as_bf16``."""
+    H = w.Hq * w.D
+    s = float(1.0 / np.sqrt(H))
+    x = draw_tensor(w.seed, T_X, w.B, 1, w.L, H, 1.0, as_bf16)[:, 0]
+    def mat(tid, rows, cols):
+        return draw_tensor(w.seed, tid, n_layers, 1, rows, cols, s, as_bf16)[:, 0]
+    g = draw_tensor(w.seed, T_G, n_layers, 1, 1, H, 0.1, as_bf16=False)[:, 0, 0]
+    g = (g + np.float32(1.0)).astype(np.float32)
+    gamma = f32_to_bf16_bits(g) if as_bf16 else g
+    wq, wk, wv = mat(T_WQ, w.Hq * w.D, H), mat(T_WK, w.Hkv * w.D, H), mat(T_WV, w.Hkv * w.D, H)
+    wo = mat(T_WO, H, w.Hq * w.D)
+    layers = [{"gamma": gamma[i], "wq": wq[i], "wk": wk[i], "wv": wv[i], "wo": wo[i]}
+              for i in range(n_layers)]
+    return {"x": x, "layers": layers}
