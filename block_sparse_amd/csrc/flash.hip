@@ -4,11 +4,11 @@
 // Phase 1 (Pith review of Star Attention, "What carries the argument"):
 // a row at position p of block i >= 1 attends to the anchor keys [0, a) and
 // to its own block's keys up to p; block 1 is plain causal attention.  The
-// anchor's K/V are block 1's K/V, read in place.  Phase 2 (same review,
-// "Circularity Check"): every KV chunk yields a local output and lse.
-// Both are written as "q rows against <= 2 key ranges, key visible iff it
-// lies in a range and its position is <= the row's position", so one kernel
-// serves both.  The mask is analytic: only tiles that cross a range end or
+// anchor's K/V are block 1's K/V, read in place (or, with a prefix table,
+// any rows of a separate pk/pv pair).  Phase 2 (same review, "Circularity
+// Check"): every KV chunk yields a local output and lse.  Both are written
+// as "q rows against <= 2 key ranges: every key of range A, and the keys of
+// range B up to the row's position", so one kernel serves both.  The mask is analytic: only tiles that cross a range end or
 // the diagonal evaluate it.
 //
 // Work decomposition.  One workgroup = NW waves; wave w owns CB column
@@ -26,7 +26,6 @@
 #include "internal.h"
 #include "flash_items.h"
 
-#include <cstdlib>
 
 namespace star {
 namespace {
@@ -378,13 +377,12 @@ hipError_t launch_cfg(FlashParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// bf16 inputs with D = 128 take the flash2 kernel; fp32 inputs (rounded to
+// bf16 on load) and D = 64 take this one.
 hipError_t launch_flash(FlashParams& p, hipStream_t stream) {
-  static const char* cfg = getenv("STAR_FLASH_CFG");
-  const bool wide = cfg != nullptr && cfg[0] == 'w';
-  const bool v1 = cfg != nullptr && cfg[0] == '1';
-  if (!wide && !v1 && flash2_supported(p)) return launch_flash2(p, stream);
-  if (p.D == 128) return wide ? launch_cfg<128, 4, 2>(p, stream) : launch_cfg<128, 8, 1>(p, stream);
-  return wide ? launch_cfg<64, 4, 2>(p, stream) : launch_cfg<64, 8, 1>(p, stream);
+  if (flash2_supported(p)) return launch_flash2(p, stream);
+  if (p.D == 128) return launch_cfg<128, 8, 1>(p, stream);
+  return launch_cfg<64, 8, 1>(p, stream);
 }
 
 }  // namespace star

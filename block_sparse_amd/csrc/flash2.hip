@@ -4,27 +4,29 @@
 // Same work decomposition and math as flash.hip (see flash_items.h for the
 // key ranges each row sees: Pith review of Star Attention, "What carries
 // the argument" and "Circularity Check"), re-planned around the costs the
-// hardware counters showed: the kernel is bound by VALU issue, not by MFMA.
-//  * K and V tiles go global -> LDS with global_load_lds_dwordx4: no staging
-//    registers, no ds_write, no VALU work.  A wave's load writes 1 KiB of
-//    LDS at consecutive addresses, so the chunk swizzle (see swz) is done by
-//    permuting the global source addresses instead.
+// hardware counters showed: the plain fp32 VALU work of the softmax (max,
+// scale, row sums, conversions) barely overlaps the MFMAs on this chip, so
+// every VALU instruction that is not softmax arithmetic is removed.
+//  * K and V tiles go global -> LDS with global_load_lds_dwordx4 from a
+//    scalar base plus a fixed per-lane offset: no staging registers, no
+//    ds_write, no per-tile address arithmetic.  A wave's load writes 1 KiB
+//    of LDS at consecutive addresses, so the chunk swizzle (see swz) is done
+//    by permuting the global source addresses instead.
 //  * V stays row-major in LDS; the V^T operand of the PV MFMA is read with
 //    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
 //    across each 16-lane group.
 //  * every LDS address is a per-lane constant plus an immediate: the tile
-//    loop is unrolled over the two buffers.
+//    loop is unrolled over the three buffers.
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
-// One workgroup = 8 waves, one 32-row column block each; 64-key tiles,
-// double-buffered; two waves share a SIMD so one's softmax overlaps the
-// other's MFMAs.
+// One workgroup = 8 waves, one 32-row column block each; 64-key tiles in
+// three LDS buffers (one tile computing, one landing, one free); two waves
+// share a SIMD so one's softmax overlaps the other's MFMAs.
 #include "common.h"
 #include "internal.h"
 #include "flash_items.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace star {
