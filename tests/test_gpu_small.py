@@ -257,3 +257,93 @@ def test_decode_step_parity(case):
     check_out(o_u[:, :, :T], ref_o, "unfused O")
     assert np.abs(o_f[:, :, :T] - o_u[:, :, :T]).max() < 2e-3
     assert np.abs(l_f[:T] - l_u[:T]).max() < 2e-4
+
+
+def test_phase1_many_small_blocks():
+    """640 blocks of 16 tokens (anchor 16): far more blocks than the prefix
+    table allows, on the analytic anchor path."""
+    B, Hq, Hkv, D, L, b = 1, 8, 2, 128, 10240, 16
+    print("phase1 640 blocks", flush=True)
+    q, k, v = _qkv(81, B, Hq, Hkv, L, D)
+    o, lse = sa.phase1_blocklocal(to_dev(q), to_dev(k), to_dev(v), b, b, want_lse=True)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(0, 48), np.arange(5000, 5040), np.arange(L - 40, L)])
+    for h in (0, 5):
+        qq = f64(q)[0, h][pos]
+        ro, rl = so.phase1_rows(qq, pos, f64(k)[0, h // 4], f64(v)[0, h // 4], b, b,
+                                1 / math.sqrt(D))
+        check_out(host64(o)[0, h][pos], ro, "O", bf16_out=True)
+        check_lse(host64(lse)[0, h][pos], rl, "LSE")
+
+
+def test_phase1_prefix_at_the_block_limit():
+    """A prefix table of STAR_MAX_PARTS = 128 blocks."""
+    B, Hq, Hkv, D, b = 1, 4, 1, 128, 32
+    L = 128 * b
+    R = 200
+    print("phase1 prefix 128 blocks", flush=True)
+    q, k, v = _qkv(82, B, Hq, Hkv, L, D)
+    pk, pv = rand_tensor(82, 3, B, Hkv, R, D), rand_tensor(82, 4, B, Hkv, R, D)
+    rng = np.random.default_rng(82)
+    st = rng.integers(0, R, size=128)
+    ln = np.array([rng.integers(0, R - s + 1) for s in st])
+    o, lse = sa.phase1_prefix(to_dev(q), to_dev(k), to_dev(v), to_dev(pk), to_dev(pv), st, ln,
+                              b, want_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = so.phase1_prefix(f64(q), f64(k), f64(v), f64(pk), f64(pv), st, ln, b,
+                                    1 / math.sqrt(D))
+    check_out(host64(o), ref_o, "O", bf16_out=True)
+    check_lse(host64(lse), ref_l, "LSE")
+    with pytest.raises(sa.StarError):                   # 133 blocks: refused before any launch
+        sa.phase1_prefix(to_dev(q), to_dev(k), to_dev(v), to_dev(pk), to_dev(pv),
+                         np.zeros(133, np.int64), np.zeros(133, np.int64), 31)
+
+
+@pytest.mark.parametrize("Lq,splits", [(1, 8), (64, 2)])
+def test_phase2_at_the_partition_limit(Lq, splits):
+    """128 partitions (the limit) x splits chunks, merged: decode and flash
+    paths; the merge combines up to 1024 partials per row."""
+    B, Hq, Hkv, D, b = 1, 8, 2, 128, 64
+    L = 128 * b - 30                                  # ragged last partition
+    print(f"phase2 128 partitions Lq={Lq} splits={splits}", flush=True)
+    N = L + Lq
+    q = rand_tensor(83, 3, B, Hq, Lq, D)
+    kc = rand_tensor(83, 4, B, Hkv, N, D)
+    vc = rand_tensor(83, 5, B, Hkv, N, D)
+    parts = so.partitions(L, b, N)
+    assert len(parts) == 128
+    offs = [p[0] for p in parts] + [parts[-1][1]]
+    op, lp = sa.phase2_partial(to_dev(q), to_dev(kc), to_dev(vc), offs, splits, q_pos0=L)
+    o, l = sa.lse_merge(op, lp)
+    torch.cuda.synchronize()
+    qpos = L + np.arange(Lq)
+    for h in (0, 7):
+        ro, rl, _, _ = so.phase2(f64(q)[0, h], qpos, f64(kc)[0, h // 4], f64(vc)[0, h // 4],
+                                 parts, 1 / math.sqrt(D))
+        check_out(host64(o)[0, h], ro, "O merged")
+        check_lse(host64(l)[0, h], rl, "LSE merged")
+
+
+def test_decode_step_max_splits():
+    """One partition cut into the maximum 1024 chunks (most of them empty)."""
+    from block_sparse_amd.pipeline import StarAttentionStep
+    B, Hq, Hkv, D, L, b = 1, 4, 1, 128, 700, 1000
+    print("decode_step splits=1024", flush=True)
+    q = rand_tensor(84, 0, B, Hq, L, D)
+    k = rand_tensor(84, 1, B, Hkv, L, D)
+    v = rand_tensor(84, 2, B, Hkv, L, D)
+    qd, kd, vd = (rand_tensor(84, t, B, H, 1, D) for t, H in ((6, Hq), (7, Hkv), (8, Hkv)))
+    st = StarAttentionStep(B, Hq, Hkv, D, L, b, 0, 1, splits_decode=1024)
+    st.load_context(to_dev(v))
+    st.rope_context(to_dev(q), to_dev(k))
+    st.decode(0, to_dev(qd), to_dev(kd), to_dev(vd))
+    torch.cuda.synchronize()
+    rot = lambda x, p: so.round_bf16(so.rope(x, p, st.base))
+    K = np.concatenate([rot(f64(k), np.arange(L)), rot(f64(kd), [L])], axis=2)
+    V = np.concatenate([f64(v), f64(vd)], axis=2)
+    qr = rot(f64(qd), [L])
+    for h in range(Hq):
+        ro, rl, _, _ = so.phase2(qr[0, h], np.array([L]), K[0, 0], V[0, 0],
+                                 so.partitions(L, b, L + 1), 1 / math.sqrt(D))
+        check_out(host64(st.od)[0, h, :1], ro, "decode O")
+        check_lse(host64(st.lsed)[0, 0, h:h + 1], rl, "decode LSE")
