@@ -15,8 +15,14 @@
 //  * V stays row-major in LDS; the V^T operand of the PV MFMA is read with
 //    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
 //    across each 16-lane group.
-//  * every LDS address is a per-lane constant plus an immediate: the tile
-//    loop is unrolled over the three buffers.
+//  * every LDS address is a per-lane register plus an immediate below
+//    64 KiB: the tile loop is unrolled over the three buffers, the K tiles
+//    and the V tiles sit in two 48 KiB arrays, and each array's address is
+//    folded into the per-lane registers, so no LDS read needs an add.
+//  * which sub-tiles need the causal / range-end mask is decided from two
+//    32-bit thresholds computed once (64-bit compares would go to the VALU).
+//  * the row max uses IEEE maximum (v_maximum3_f32), which needs no
+//    canonicalisation of the MFMA results first.
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
@@ -37,7 +43,6 @@ constexpr int NW = 8;
 constexpr int KT = 64;
 constexpr int ROWB = D * 2;                 // bytes per K/V row
 constexpr int TILE = KT * ROWB;             // 16 KiB
-constexpr int BUF = 2 * TILE;               // K tile + V tile
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int NBUF = 3;                     // LDS tile buffers
 
@@ -81,21 +86,23 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
 }
 
-__device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(int addr) {
+  return (const __attribute__((address_space(3))) T*)(uintptr_t)(uint32_t)addr;
+}
+
+__device__ __forceinline__ s16x4 tr_read(int addr) {
 #if __HIP_DEVICE_COMPILE__
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(uint32_t)addr);
 #else
   return s16x4{0, 0, 0, 0};
 #endif
 }
 
 __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
-  // three separate LDS objects, so that the compiler can tell a DMA into
-  // one buffer from reads of another and does not wait for it
-  __shared__ __attribute__((aligned(1024))) uint8_t sm0[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm1[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm2[BUF];
-  auto buf_ptr = [&](int b) -> uint8_t* { return b == 0 ? sm0 : (b == 1 ? sm1 : sm2); };
+  // tile buffer b: K rows at smK + b TILE, V rows at smV + b TILE
+  __shared__ __attribute__((aligned(1024))) uint8_t smK[NBUF * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smV[NBUF * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,7 +152,10 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // K read for S^T: row 32kb + l32, logical chunk 2dc + hf
   int kofs[D / 16];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) kofs[dc] = l32 * ROWB + (((2 * dc + hf) ^ swz(l32)) << 4);
+  for (int dc = 0; dc < D / 16; ++dc) {
+    kofs[dc] = (int)lds_u32(smK) + l32 * ROWB + (((2 * dc + hf) ^ swz(l32)) << 4);
+    asm("" : "+v"(kofs[dc]));   // keep the array address in the register
+  }
   // V^T via transpose reads: 16-lane group G = lane >> 4 (h = G >> 1 selects
   // keys 4h.., gsub = G & 1 selects d 16gsub..), lane j = lane & 15 points at
   // row (8t + 4h + (j >> 2)) and columns 32db + 16gsub + 4(j & 3) .. +3
@@ -158,7 +168,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int c = 4 * db + 2 * gsub + ((j & 3) >> 1);
-        vofs[t][db] = rr * ROWB + ((c ^ swz(rr)) << 4) + 8 * (j & 1);
+        vofs[t][db] = (int)lds_u32(smV) + rr * ROWB + ((c ^ swz(rr)) << 4) + 8 * (j & 1);
+        asm("" : "+v"(vofs[t][db]));
       }
     }
   }
@@ -208,7 +219,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     const bool full = r0 + KT <= rows;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(buf_ptr(buf) + (8 * wave + 4 * i) * ROWB));
+      const int at = buf * TILE + (8 * wave + 4 * i) * ROWB;
+      const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(smK + at));
+      const uint32_t dv = __builtin_amdgcn_readfirstlane(lds_u32(smV + at));
       uint32_t okk = ok[i], ovv = ov[i];
       if (!full) {
         const int64_t rr = min(r0 + lrow[i], rows - 1) - r0;
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
         ovv = (uint32_t)(rr * vs + lcolb[i]);
       }
       dma16(kb, okk, dk);
-      dma16(vb, ovv, dk + TILE);
+      dma16(vb, ovv, dv);
     }
   };
   // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it)
@@ -236,16 +249,15 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 
   // Sub-tile j (32 keys) lives in LDS buffer (j / 2) % 3, rows 32 (j % 2) ..
   // The loop below is unrolled over the 6 sub-tiles of one buffer cycle so
-  // that every LDS address is a per-lane constant plus an immediate.
+  // that every LDS address is a per-lane register plus an immediate.
   auto qk = [&](auto boff) -> f32x16 {
     constexpr int OFF = decltype(boff)::value;
-    const uint8_t* base = buf_ptr(OFF / BUF) + OFF % BUF;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
-      s = mfma32(*reinterpret_cast<const bf16x8*>(base + kofs[dc]), qf[dc], s);
+      s = mfma32(*lds_ptr<bf16x8>(kofs[dc] + OFF), qf[dc], s);
     return s;
   };
   // first key of sub-tile j, relative to the start of its key range, and
@@ -256,11 +268,20 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   };
   // keys of sub-tile j past the range end or (range B only) after the row's
   // position -> -inf
+  // first sub-tile of each range that needs the mask: range A's sub-tiles
+  // reaching past its end; range B's reaching past its end or past the
+  // wave's first query position
+  const int jmA = (int)((it.ra1 - it.ra0) >> 5);
+  int jmB;
+  {
+    const int64_t xb = wave_min - 31 - it.rb0;
+    jmB = 2 * nt0 + (int)min((it.rb1 - it.rb0) >> 5, xb < 0 ? (int64_t)0 : (xb >> 5) + 1);
+  }
   auto mask = [&](int j, f32x16& s) {
-    const int64_t ks = sub_key(j);
-    const bool A = (j >> 1) < nt0;
-    const int64_t rend = A ? it.ra1 : it.rb1;
-    if (ks + 32 > rend || (!A && ks + 31 > wave_min)) {
+    const bool A = j < 2 * nt0;
+    if (__builtin_expect(j >= (A ? jmA : jmB), 0)) {
+      const int64_t ks = sub_key(j);
+      const int64_t rend = A ? it.ra1 : it.rb1;
       const int lim_end = (int)min(rend - ks, (int64_t)32);
       const int lim_pos = A ? 32 : (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
 #pragma unroll
@@ -285,17 +306,17 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2)
   auto step = [&](auto jjc, int j) {
     constexpr int JJ = decltype(jjc)::value;
-    constexpr int CUR = (JJ >> 1) * BUF + (JJ & 1) * 32 * ROWB;          // this sub-tile
+    constexpr int CUR = (JJ >> 1) * TILE + (JJ & 1) * 32 * ROWB;         // this sub-tile
     constexpr int JN = (JJ + 1) % 6;
-    constexpr int NXT = (JN >> 1) * BUF + (JN & 1) * 32 * ROWB;          // the next one
+    constexpr int NXT = (JN >> 1) * TILE + (JN & 1) * 32 * ROWB;         // the next one
     // row max of S_j (16 values in the lane + the partner half), lazy rescale
     float mt = s[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, s[r]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const float mt2 = mt * c2;
     const bool need = mt2 > m2 + kRescaleLog2;
@@ -338,9 +359,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const uint8_t* vb = buf_ptr(CUR / BUF) + CUR % BUF + TILE + cc * 16 * ROWB;
-        const s16x4 a0 = tr_read(vb + vofs[0][db]);
-        const s16x4 a1 = tr_read(vb + vofs[1][db]);
+        const s16x4 a0 = tr_read(vofs[0][db] + CUR + cc * 16 * ROWB);
+        const s16x4 a1 = tr_read(vofs[1][db] + CUR + cc * 16 * ROWB);
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pf[cc], oacc[db]);
