@@ -23,6 +23,9 @@
 //    32-bit thresholds computed once (64-bit compares would go to the VALU).
 //  * the row max uses IEEE maximum (v_maximum3_f32), which needs no
 //    canonicalisation of the MFMA results first.
+//  * each 32-key step is one basic block (exp of S_j, QK of S_{j+1}, PV of
+//    P_j, row max of S_{j+1}); the rare branches (mask, rescale) follow it,
+//    and the rescale test needs no cross-lane max unless it fires.
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
@@ -277,18 +280,51 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     const int64_t xb = wave_min - 31 - it.rb0;
     jmB = 2 * nt0 + (int)min((it.rb1 - it.rb0) >> 5, xb < 0 ? (int64_t)0 : (xb >> 5) + 1);
   }
+  auto mask_needed = [&](int j) -> bool { return j >= (j < 2 * nt0 ? jmA : jmB); };
   auto mask = [&](int j, f32x16& s) {
     const bool A = j < 2 * nt0;
-    if (__builtin_expect(j >= (A ? jmA : jmB), 0)) {
-      const int64_t ks = sub_key(j);
-      const int64_t rend = A ? it.ra1 : it.rb1;
-      const int lim_end = (int)min(rend - ks, (int64_t)32);
-      const int lim_pos = A ? 32 : (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
+    const int64_t ks = sub_key(j);
+    const int64_t rend = A ? it.ra1 : it.rb1;
+    const int lim_end = (int)min(rend - ks, (int64_t)32);
+    const int lim_pos = A ? 32 : (int)max(min(qpos - ks, (int64_t)32), (int64_t)-1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key >= lim_end || key > lim_pos) s[r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= lim_end || key > lim_pos) s[r] = -INFINITY;
+    }
+  };
+  auto rowmax = [&](const f32x16& sv) -> float {
+    float ml = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) ml = __builtin_elementwise_maximum(ml, sv[r]);
+    return ml;
+  };
+
+  // Lazy online softmax: m2 (log2 units) changes only when a column's max
+  // grows past m2 + 8, and only then are O and the row sum rescaled.  The
+  // test runs on the lane's own 16 keys against thr = (m2 + 8) / c (scale
+  // > 0); only a wave that takes the rare branch forms the full column max
+  // across the two lane halves.
+  const float inv_c2 = 1.0f / c2;
+  float thr = -INFINITY;
+  auto rescale_if_needed = [&](float ml, bool live) {
+    if (__builtin_expect(__any(ml > thr), 0)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ml), __float_as_uint(ml),
+                                                       false, false);
+      const float mt2 =
+          __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+      const bool need = live && mt2 > m2 + kRescaleLog2;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
+      if (need) {
+        m2 = mt2;
+        msub = mt2;
+        thr = (mt2 + kRescaleLog2) * inv_c2;
       }
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
   };
 
@@ -300,38 +336,17 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   f32x16 s = {};
   if (nsub > 0) {
     s = qk(std::integral_constant<int, 0>{});
-    mask(0, s);
+    if (mask_needed(0)) mask(0, s);
+    rescale_if_needed(rowmax(s), true);
   }
 
-  // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2)
+  // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2).
+  // On entry s = S_j, masked, with m2 already covering it.
   auto step = [&](auto jjc, int j) {
     constexpr int JJ = decltype(jjc)::value;
     constexpr int CUR = (JJ >> 1) * TILE + (JJ & 1) * 32 * ROWB;         // this sub-tile
     constexpr int JN = (JJ + 1) % 6;
     constexpr int NXT = (JN >> 1) * TILE + (JN & 1) * 32 * ROWB;         // the next one
-    // row max of S_j (16 values in the lane + the partner half), lazy rescale
-    float mt = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, s[r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                       false, false);
-      mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt2 = mt * c2;
-    const bool need = mt2 > m2 + kRescaleLog2;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
-      if (need) {
-        m2 = mt2;
-        msub = mt2;
-      }
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
     const bool more = j + 1 < nsub;
     if constexpr ((JJ & 1) == 1) {
       // the next sub-tile starts a new tile: make it resident, then put the
@@ -343,9 +358,10 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
         if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tn);
       }
     }
-    // P_j = exp2(S_j c - m): fp32 for the denominator, bf16 for PV; issued
-    // together with the next sub-tile's QK MFMAs (unconditional so they
-    // share a basic block; after the last sub-tile the result is unused)
+    // One basic block: P_j = exp2(S_j c - m) (fp32 for the denominator, bf16
+    // for PV), the QK MFMAs of S_{j+1}, O^T += V^T P^T and the row max of
+    // S_{j+1}, so the scheduler can put VALU work under every MFMA.  After
+    // the last sub-tile S_{j+1} is unused (its slot may hold stale data).
     bf16x8 pf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -354,7 +370,6 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
       pf[e >> 3][e & 7] = (__bf16)pv;
     }
     f32x16 sn = qk(std::integral_constant<int, NXT>{});
-    // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -365,7 +380,16 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pf[cc], oacc[db]);
       }
-    if (more) mask(j + 1, sn);
+    float ml = rowmax(sn);
+    // keep the row-sum adds in this block (they would otherwise be sunk
+    // past the branch below, as one serial chain with no MFMA to hide under)
+    asm volatile("" : "+v"(lsum));
+    // masking only lowers scores: the masked max replaces the unmasked one
+    if (__builtin_expect(more && mask_needed(j + 1), 0)) {
+      mask(j + 1, sn);
+      ml = __builtin_elementwise_minimum(ml, rowmax(sn));
+    }
+    rescale_if_needed(ml, more);
     s = sn;
   };
 
