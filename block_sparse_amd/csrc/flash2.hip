@@ -5,8 +5,9 @@
 // key ranges each row sees: Pith review of Star Attention, "What carries
 // the argument" and "Circularity Check"), re-planned around the costs the
 // hardware counters showed: the plain fp32 VALU work of the softmax (max,
-// scale, row sums, conversions) barely overlaps the MFMAs on this chip, so
-// every VALU instruction that is not softmax arithmetic is removed.
+// scale, row sums, conversions) does not overlap the MFMAs of its SIMD on
+// this chip (only the exps do), so every VALU instruction that is not
+// softmax arithmetic is removed, and so is the row max of the common path.
 //  * K and V tiles go global -> LDS with global_load_lds_dwordx4 from a
 //    scalar base plus a fixed per-lane offset: no staging registers, no
 //    ds_write, no per-tile address arithmetic.  A wave's load writes 1 KiB
@@ -21,17 +22,21 @@
 //    folded into the per-lane registers, so no LDS read needs an add.
 //  * which sub-tiles need the causal / range-end mask is decided from two
 //    32-bit thresholds computed once (64-bit compares would go to the VALU).
-//  * the row max uses IEEE maximum (v_maximum3_f32), which needs no
-//    canonicalisation of the MFMA results first.
-//  * each 32-key step is one basic block (exp of S_j, QK of S_{j+1}, PV of
-//    P_j, row max of S_{j+1}); the rare branches (mask, rescale) follow it,
-//    and the rescale test needs no cross-lane max unless it fires.
+//  * lazy online softmax tested after the fact: P_j is formed with the
+//    current shift, and the lane's sum of its 16 values (needed for the
+//    denominator anyway) exceeding 2^8 is the sign that some score passed
+//    the shift by more than 8 (log2 units).  Only then is the column max
+//    formed (IEEE maximum, v_maximum3_f32: no canonicalisation of the MFMA
+//    results), O rescaled and P_j recomputed.  Per 32 keys a wave issues
+//    16 MFMAs and 57 other VALU instructions (16 FMA, 16 exp, 16 adds,
+//    8 packs, 1 compare).
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
 // One workgroup = 8 waves, one 32-row column block each; 64-key tiles in
 // three LDS buffers (one tile computing, one landing, one free); two waves
-// share a SIMD so one's softmax overlaps the other's MFMAs.
+// share a SIMD, so one's LDS reads, barrier waits and exps run under the
+// other's MFMAs.
 #include "common.h"
 #include "internal.h"
 #include "flash_items.h"
@@ -47,6 +52,7 @@ constexpr int KT = 64;
 constexpr int ROWB = D * 2;                 // bytes per K/V row
 constexpr int TILE = KT * ROWB;             // 16 KiB
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleP = 256.0f;          // 2^kRescaleLog2
 constexpr int NBUF = 3;                     // LDS tile buffers
 
 // s_waitcnt vmcnt(4): all but this wave's last 4 vector-memory ops done
@@ -293,40 +299,31 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
       if (key >= lim_end || key > lim_pos) s[r] = -INFINITY;
     }
   };
-  auto rowmax = [&](const f32x16& sv) -> float {
+  // column max of S across the lane's 16 keys and the partner half's 16
+  auto colmax = [&](const f32x16& sv) -> float {
     float ml = sv[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) ml = __builtin_elementwise_maximum(ml, sv[r]);
-    return ml;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ml), __float_as_uint(ml),
+                                                     false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // P = exp2(S c - msub) of one sub-tile: the bf16 operand of PV, and the
+  // sum of the lane's 16 fp32 values (returned)
+  auto softmax_p = [&](const f32x16& sv, bf16x8* pf) -> float {
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c2, -msub));
+      ls += pv;
+      pf[e >> 3][e & 7] = (__bf16)pv;
+    }
+    return ls;
   };
 
-  // Lazy online softmax: m2 (log2 units) changes only when a column's max
-  // grows past m2 + 8, and only then are O and the row sum rescaled.  The
-  // test runs on the lane's own 16 keys against thr = (m2 + 8) / c (scale
-  // > 0); only a wave that takes the rare branch forms the full column max
-  // across the two lane halves.
-  const float inv_c2 = 1.0f / c2;
-  float thr = -INFINITY;
-  auto rescale_if_needed = [&](float ml, bool live) {
-    if (__builtin_expect(__any(ml > thr), 0)) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ml), __float_as_uint(ml),
-                                                       false, false);
-      const float mt2 =
-          __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
-      const bool need = live && mt2 > m2 + kRescaleLog2;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
-      if (need) {
-        m2 = mt2;
-        msub = mt2;
-        thr = (mt2 + kRescaleLog2) * inv_c2;
-      }
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-  };
+  // lane-sum limit that triggers the rescale test: -1 (always) until the
+  // column has a finite max, then 2^8
+  float plim = -1.f;
 
   // prologue: tiles 0 and 1 in flight, wait for tile 0, first S
   if (nt > 0) load_tile(0, 0);
@@ -337,11 +334,10 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   if (nsub > 0) {
     s = qk(std::integral_constant<int, 0>{});
     if (mask_needed(0)) mask(0, s);
-    rescale_if_needed(rowmax(s), true);
   }
 
   // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2).
-  // On entry s = S_j, masked, with m2 already covering it.
+  // On entry s = S_j, masked.
   auto step = [&](auto jjc, int j) {
     constexpr int JJ = decltype(jjc)::value;
     constexpr int CUR = (JJ >> 1) * TILE + (JJ & 1) * 32 * ROWB;         // this sub-tile
@@ -358,18 +354,38 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
         if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tn);
       }
     }
-    // One basic block: P_j = exp2(S_j c - m) (fp32 for the denominator, bf16
-    // for PV), the QK MFMAs of S_{j+1}, O^T += V^T P^T and the row max of
-    // S_{j+1}, so the scheduler can put VALU work under every MFMA.  After
-    // the last sub-tile S_{j+1} is unused (its slot may hold stale data).
+    // P_j with the current shift, issued together with the QK MFMAs of
+    // S_{j+1} (after the last sub-tile S_{j+1} is unused: its slot may hold
+    // stale data)
     bf16x8 pf[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, -msub));
-      lsum += pv;
-      pf[e >> 3][e & 7] = (__bf16)pv;
-    }
+    float ls = softmax_p(s, pf);
     f32x16 sn = qk(std::integral_constant<int, NXT>{});
+    // Lazy rescale, tested after the fact: a column whose scores exceed
+    // its shift by more than 8 (log2 units) has a P above 2^8, so its lane
+    // sum exceeds 2^8.  Only a wave where some lane's sum exceeds plim
+    // (or where a column has seen no finite score yet) forms the column max; columns
+    // whose max grew by more than 8 rescale O and the row sum and
+    // recompute P_j.
+    if (__builtin_expect(__any(ls > plim), 0)) {
+      const float mt2 = colmax(s) * c2;
+      const bool need = mt2 > m2 + kRescaleLog2;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mt2) : 1.0f;
+        if (need) {
+          m2 = mt2;
+          msub = mt2;
+          plim = kRescaleP;
+        }
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        ls = softmax_p(s, pf);
+      }
+    }
+    lsum += ls;
+    // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -380,16 +396,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pf[cc], oacc[db]);
       }
-    float ml = rowmax(sn);
-    // keep the row-sum adds in this block (they would otherwise be sunk
-    // past the branch below, as one serial chain with no MFMA to hide under)
-    asm volatile("" : "+v"(lsum));
-    // masking only lowers scores: the masked max replaces the unmasked one
-    if (__builtin_expect(more && mask_needed(j + 1), 0)) {
-      mask(j + 1, sn);
-      ml = __builtin_elementwise_minimum(ml, rowmax(sn));
-    }
-    rescale_if_needed(ml, more);
+    if (__builtin_expect(more && mask_needed(j + 1), 0)) mask(j + 1, sn);
     s = sn;
   };
 
