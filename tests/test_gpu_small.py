@@ -50,6 +50,34 @@ def test_phase1_parity(case):
     check_lse(host64(lse), ref_l, "LSE")
 
 
+# (q scale, k scale at position 0, k scale at the last position)
+RESCALE_CASES = [(2.0, 2.0, 8.0), (2.0, 8.0, 2.0), (6.0, 6.0, 6.0)]
+
+
+@pytest.mark.parametrize("case", RESCALE_CASES, ids=["growing", "shrinking", "overflow"])
+def test_phase1_rescale_stress(case):
+    """Large scores for the lazy online softmax: scores that keep growing
+    along the keys (the running max passes its shift many times), that keep
+    shrinking, and that are large enough (std ~52 in log2 units) that P of
+    the first sub-tile, formed before any shift is known, overflows fp32.
+    V is drawn at scale 0.5 so that the bf16 rounding of P (2^-9 of each
+    weight) stays inside the output bound when the attention is peaked."""
+    qs, k0, k1 = case
+    B, Hq, Hkv, D, L, b, a = 1, 8, 2, 128, 1100, 300, 300
+    print(f"phase1 rescale case {case}", flush=True)
+    q = so.round_bf16(rand_tensor(41, 0, B, Hq, L, D, qs, False).astype(np.float64))
+    ramp = np.linspace(k0, k1, L)[None, None, :, None]
+    k = so.round_bf16(rand_tensor(41, 1, B, Hkv, L, D, 1.0, False).astype(np.float64) * ramp)
+    v = so.round_bf16(rand_tensor(41, 2, B, Hkv, L, D, 0.5, False).astype(np.float64))
+    dev = lambda t: to_dev(t.astype(np.float32)).to(torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    o, lse = sa.phase1_blocklocal(dev(q), dev(k), dev(v), b, a, want_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = so.phase1(q, k, v, b, a, scale)
+    check_out(host64(o), ref_o, "O", bf16_out=True)
+    check_lse(host64(lse), ref_l, "LSE")
+
+
 P2_CASES = [
     # B, Hq, Hkv, D, L, Lq, b, splits
     (1, 2, 1, 64, 512, 16, 128, 1),     # tiny workload query phase (flash path)
