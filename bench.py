@@ -252,6 +252,37 @@ def decode_cold(st, dev, w, ev, samples=16):
             "note": "each step after a 1 GiB read that flushes L2 and Infinity Cache"}
 
 
+def hbm_stream(ev, mib=1024, reps=5):
+    """Achievable streaming-read rate on this GPU: the library's plain
+    streaming read (16-byte loads, every byte once) over 1 GiB, four times
+    the 256 MiB Infinity Cache, so every pass reads HBM; best of three grid
+    sizes.  Reported beside the decode rate as the practical ceiling of an
+    HBM-bound kernel."""
+    import torch
+
+    import block_sparse_amd as sa
+
+    buf = torch.ones(mib << 18, dtype=torch.int32, device="cuda")
+    best = None
+    for wg in (2048, 4096, 8192):
+        out = torch.empty(wg, dtype=torch.int32, device="cuda")
+        sa.stream_read(buf, wg, out)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            sa.stream_read(buf, wg, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        if best is None or ms < best[0]:
+            best = (ms, wg)
+    gbps = (mib << 20) / (best[0] * 1e-3) / 1e9
+    del buf
+    return {"gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBS, "bytes": mib << 20,
+            "workgroups": best[1],
+            "note": "star_stream_read over 1 GiB (a plain streaming read, 16-byte loads)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +401,8 @@ def main():
                                  "K+V bytes of every visible token"}
     if not args.phase1_only and w.T > 0 and not args.no_cold:
         out["decode_cold"] = decode_cold(st, dev, w, ev)
+    if not args.phase1_only and w.T > 0:
+        out["hbm_stream"] = hbm_stream(ev)
     if w.rope and not args.no_variants:
         out["phase1_variants"] = phase1_variants(st, dev, w, x, ev)
     if not args.no_layer:

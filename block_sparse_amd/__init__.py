@@ -23,7 +23,7 @@ from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
 __all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_prefix",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
-           "Context", "rmsnorm", "linear", "split_ranges",
+           "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
            "StarError", "library"]
 
 
@@ -159,6 +159,20 @@ def gather_rows(src, rows, out=None):
     a, b = _desc(src), _desc(out)
     st = library().star_gather_rows(ctypes.byref(a), _ptr(rows), ctypes.byref(b), _stream(src))
     _lib.check("star_gather_rows", st)
+    return out
+
+
+def stream_read(buf: torch.Tensor, workgroups: int = 4096, out=None):
+    """Plain streaming read of ``buf`` (a measurement aid, not a step of the
+    method): returns the per-workgroup XOR of the 32-bit words read, device
+    uint32 [workgroups] as int32."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if out is None:
+        out = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    st = library().star_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                    int(workgroups), _ptr(out), _stream(buf))
+    _lib.check("star_stream_read", st)
     return out
 
 

@@ -166,7 +166,7 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 200; }
+int star_abi_version(void) { return 201; }
 
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
                     int64_t pos0, double base, void* stream) {
@@ -326,6 +326,19 @@ int star_phase1_prefix(const star_tensor* q, const star_tensor* k, const star_te
     p.chunk[i] = prefix_len[i];
   }
   return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_stream_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                     void* stream) {
+  if (src == nullptr || out == nullptr) return STAR_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+    return STAR_ERR_ALIGN;
+  if (workgroups < 1 || workgroups > 65536 || bytes <= 0) return STAR_ERR_SHAPE;
+  const int64_t unit = star::stream_read_granule() * workgroups;
+  if (bytes % unit != 0) return STAR_ERR_SHAPE;
+  return hip_status(star::launch_stream_read(src, bytes, workgroups, out,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int star_gather_rows(const star_tensor* src, const int64_t* rows, const star_tensor* dst,

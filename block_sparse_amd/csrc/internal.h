@@ -150,6 +150,12 @@ struct GatherParams {
 
 hipError_t launch_gather(GatherParams& p, hipStream_t stream);
 
+// streaming-read reference (stream.hip): bytes must be a multiple of
+// workgroups * stream_read_granule()
+int64_t stream_read_granule();
+hipError_t launch_stream_read(const void* src, int64_t bytes, int32_t workgroups,
+                              uint32_t* out, hipStream_t stream);
+
 // RMSNorm of every row (length D) of a [B, H, S, D] bf16 tensor
 struct RmsParams {
   TensorRef x;

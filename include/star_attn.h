@@ -347,6 +347,22 @@ int star_rmsnorm(const star_tensor* x, const void* gamma, float eps,
 int star_linear(star_context* ctx, const star_tensor* x, const star_tensor* w,
                 const star_tensor* residual, const star_tensor* y, void* stream);
 
+/*
+ * Measurement aid, not a step of the method: a plain streaming read of
+ * `bytes` bytes of device memory at `src` (each byte once, 16-byte loads).
+ * Workgroup i reads bytes [i, i + 1) * bytes / workgroups and writes the XOR
+ * of the 32-bit words it read to out[i], so the XOR of out[0 .. workgroups)
+ * is the XOR of every word of the buffer.  Its rate is the practical
+ * ceiling for the HBM-bound decode kernel on the GPU it runs on.
+ *   src         device, 16-byte aligned.
+ *   bytes       > 0, a multiple of workgroups * 32768.
+ *   workgroups  1 .. 65536.
+ *   out         device uint32 [workgroups], 4-byte aligned.
+ * Errors: STAR_ERR_NULL, STAR_ERR_ALIGN, STAR_ERR_SHAPE (sizes above).
+ */
+int star_stream_read(const void* src, int64_t bytes, int32_t workgroups,
+                     uint32_t* out, void* stream);
+
 /* Human-readable name of a star_status value (static storage). */
 const char* star_status_string(int status);
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 200
+    assert lib.star_abi_version() == 201
 
 
 def test_status_strings(lib):
@@ -193,6 +193,21 @@ def test_gather_validation(lib):
     assert g(d=T(B=1, H=3, S=7, D=128)) == -2
     assert g(d=T(B=1, H=2, S=7, D=64)) == -2
     assert g(d=T(B=1, H=2, S=0, D=128), rows=None) == 0
+
+
+def test_stream_read_validation(lib):
+    """Argument checks of the streaming-read aid (all before any launch)."""
+    fake = ctypes.c_void_p(FAKE)
+    r = lambda src=fake, n=1 << 20, wg=32, out=fake: lib.star_stream_read(src, n, wg, out, None)
+    assert r(src=None) == -1
+    assert r(out=None) == -1
+    assert r(src=ctypes.c_void_p(FAKE + 8)) == -4
+    assert r(out=ctypes.c_void_p(FAKE + 2)) == -4
+    assert r(wg=0) == -2
+    assert r(wg=65537) == -2
+    assert r(n=0) == -2
+    assert r(n=(1 << 20) + 16) == -2          # not a multiple of 32 * 32768
+    assert r(n=32768 * 31, wg=32) == -2
 
 
 def test_pulsar_prefix_host_matches_oracle(lib):

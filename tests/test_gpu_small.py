@@ -78,6 +78,18 @@ def test_phase1_rescale_stress(case):
     check_lse(host64(lse), ref_l, "LSE")
 
 
+@pytest.mark.parametrize("wg,mib", [(64, 4), (1, 1), (4096, 128)])
+def test_stream_read_checksum(wg, mib):
+    """The streaming-read aid reads every 32-bit word once: workgroup i's
+    result is the XOR of the words of slice i (bit-exact)."""
+    g = torch.Generator().manual_seed(wg)
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (mib << 18,), dtype=torch.int32, generator=g)
+    out = sa.stream_read(words.cuda(), workgroups=wg)
+    torch.cuda.synchronize()
+    ref = np.bitwise_xor.reduce(words.numpy().view(np.uint32).reshape(wg, -1), axis=1)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+
+
 P2_CASES = [
     # B, Hq, Hkv, D, L, Lq, b, splits
     (1, 2, 1, 64, 512, 16, 128, 1),     # tiny workload query phase (flash path)
