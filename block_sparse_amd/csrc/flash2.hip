@@ -10,7 +10,8 @@
 // softmax arithmetic is removed, and so is the row max of the common path.
 //  * K and V tiles go global -> LDS with global_load_lds_dwordx4 from a
 //    scalar base plus a fixed per-lane offset: no staging registers, no
-//    ds_write, no per-tile address arithmetic.  A wave's load writes 1 KiB
+//    ds_write, and per tile only a 64-bit scalar add per base (tiles load in
+//    order, so the loader advances running pointers).  A wave's load writes 1 KiB
 //    of LDS at consecutive addresses, so the chunk swizzle (see swz) is done
 //    by permuting the global source addresses instead.
 //  * V stays row-major in LDS; the V^T operand of the PV MFMA is read with
@@ -214,37 +215,67 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
   const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
   const int nsub = 2 * nt;                        // 32-key sub-tiles
-  auto tile_start = [&](int t) -> int64_t {
-    return t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0);
-  };
 
-  // the 4 DMAs of one tile whose first row is r0 rows into its range; rows
-  // past the source's end (last tile only) are clamped to its last row and
-  // masked later
-  auto issue = [&](int buf, const uint8_t* kb, const uint8_t* vb, int64_t ks, int64_t vs,
-                   const uint32_t* ok, const uint32_t* ov, int64_t r0, int64_t rows) {
-    kb += r0 * ks;
-    vb += r0 * vs;
-    const bool full = r0 + KT <= rows;
+  // Tiles are loaded in order, range A's then range B's.  The loader keeps
+  // the next tile's K and V row pointers (advanced by one 64-bit add per
+  // tile), the strides and lane offsets of its range, the number of tiles
+  // left in the range and how many of them lie wholly inside the source
+  // tensor.  Rows past the source's end (last tile only) are clamped to its
+  // last row and masked later.
+  const uint8_t* lk = kbA;
+  const uint8_t* lv = vbA;
+  int64_t lks = ksA, lvs = vsA, lrows = rowsA;
+  uint32_t lok[2] = {okA[0], okA[1]}, lov[2] = {ovA[0], ovA[1]};
+  int lleft = nt0;
+  int lfull = (int)min((int64_t)nt0, rowsA / KT);
+  bool in_a = true;
+  auto to_range_b = [&]() {
+    lk = kbB;
+    lv = vbB;
+    lks = ksB;
+    lvs = vsB;
+    lrows = rowsB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lok[i] = okB[i];
+      lov[i] = ovB[i];
+    }
+    lleft = nt - nt0;
+    lfull = (int)min((int64_t)(nt - nt0), rowsB / KT);
+    in_a = false;
+  };
+  if (nt0 == 0) to_range_b();
+  // the 4 DMAs of the next tile into buffer buf (every wave issues exactly 4
+  // loads per tile: wait_vm_keep4 relies on it)
+  auto load_next = [&](int buf) {
+    uint32_t dk[2], dv[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int at = buf * TILE + (8 * wave + 4 * i) * ROWB;
-      const uint32_t dk = __builtin_amdgcn_readfirstlane(lds_u32(smK + at));
-      const uint32_t dv = __builtin_amdgcn_readfirstlane(lds_u32(smV + at));
-      uint32_t okk = ok[i], ovv = ov[i];
-      if (!full) {
-        const int64_t rr = min(r0 + lrow[i], rows - 1) - r0;
-        okk = (uint32_t)(rr * ks + lcolb[i]);
-        ovv = (uint32_t)(rr * vs + lcolb[i]);
-      }
-      dma16(kb, okk, dk);
-      dma16(vb, ovv, dv);
+      dk[i] = __builtin_amdgcn_readfirstlane(lds_u32(smK + at));
+      dv[i] = __builtin_amdgcn_readfirstlane(lds_u32(smV + at));
     }
-  };
-  // every wave issues exactly 4 loads per tile (wait_vm_keep4 relies on it)
-  auto load_tile = [&](int buf, int t) {
-    if (t < nt0) issue(buf, kbA, vbA, ksA, vsA, okA, ovA, (int64_t)KT * t, rowsA);
-    else issue(buf, kbB, vbB, ksB, vsB, okB, ovB, (int64_t)KT * (t - nt0), rowsB);
+    if (__builtin_expect(lfull > 0, 1)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        dma16(lk, lok[i], dk[i]);
+        dma16(lv, lov[i], dv[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t rr = min((int64_t)lrow[i], lrows - 1);
+        dma16(lk, (uint32_t)(rr * lks + lcolb[i]), dk[i]);
+        dma16(lv, (uint32_t)(rr * lvs + lcolb[i]), dv[i]);
+      }
+    }
+    lk += KT * lks;
+    lv += KT * lvs;
+    lrows -= KT;
+    // wave-uniform counters: keep them in scalar registers
+    lfull = __builtin_amdgcn_readfirstlane(lfull - 1);
+    lleft = __builtin_amdgcn_readfirstlane(lleft - 1);
+    if (__builtin_expect(lleft == 0 && in_a, 0)) to_range_b();
   };
 
   f32x16 oacc[D / 32];
@@ -326,8 +357,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   float plim = -1.f;
 
   // prologue: tiles 0 and 1 in flight, wait for tile 0, first S
-  if (nt > 0) load_tile(0, 0);
-  if (nt > 1) load_tile(1, 1);
+  if (nt > 0) load_next(0);
+  if (nt > 1) load_next(1);
   if (nt > 1) wait_vm_keep4(); else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 s = {};
@@ -351,7 +382,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const int tn = (j >> 1) + 2;
-        if (tn < nt) load_tile(((JJ >> 1) + 2) % NBUF, tn);
+        if (tn < nt) load_next(((JJ >> 1) + 2) % NBUF);
       }
     }
     // P_j with the current shift, issued together with the QK MFMAs of
