@@ -137,6 +137,14 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const T* vbase = reinterpret_cast<const T*>(p.v.data) + (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH;
 
   const int nt = (int)((c1 - c0 + KTD - 1) / KTD);
+  // Workgroups start their walk at evenly spread tiles of their chunks.
+  // Chunks begin at equally aligned addresses and all workgroups stream at
+  // the same rate, so walking them in lockstep would keep hitting the same
+  // HBM channels (measured: 3-4% slower per decode step).  Tile order does
+  // not change the result beyond rounding: each wave merges its tiles with
+  // the online softmax.
+  const int rot = nt > 0 ? (int)(((int64_t)lid * nt) / (p.total_items > 0 ? p.total_items : 1)) : 0;
+  auto phys = [&](int t) { const int u = t + rot; return u >= nt ? u - nt : u; };
   uint8_t* vs = smem + wave * VT;
 
   // LDS offsets: row writes (row 16kb + n, chunk 4dc + kg) and transpose
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   // register staging, two tiles deep: [slot][key block (16 keys)][d chunk]
   u32x4 kr[2][2][NDC], vr[2][2][NDC];
   auto load_tile = [&](int slot, int t) {
-    const int64_t kt = c0 + (int64_t)KTD * t;
+    const int64_t kt = c0 + (int64_t)KTD * phys(t);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int64_t key = kt + 16 * kb + n;
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   // two steps ahead right after its registers are consumed
   auto process = [&](auto slc, int t) {
     constexpr int SL = decltype(slc)::value;
-    const int64_t kt = c0 + (int64_t)KTD * t;
+    const int64_t kt = c0 + (int64_t)KTD * phys(t);
     // S^T = K Q^T for two 16-key blocks
     f32x4 s[2];
 #pragma unroll
