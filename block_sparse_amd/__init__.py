@@ -21,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
-__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_prefix",
+__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
+           "phase1_prefix",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
            "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
            "StarError", "library"]
@@ -114,6 +115,32 @@ def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,
         ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(block_b), int(anchor_len),
         float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
     _lib.check("star_phase1_blocklocal", st)
+    return out, lse
+
+
+def phase1_rope(q, k, v, block_b: int, anchor_len: int | None = None,
+                base: float = 500000.0, scale: float | None = None, out=None, lse=None,
+                want_lse: bool = False):
+    """Phase 1 with the RoPE of ``q`` fused in: ``q`` holds un-rotated rows
+    (rotated in the kernel at positions 0..L-1), ``k`` is already rotated.
+    bf16, D = 128.  Returns ``(o, lse)`` like :func:`phase1_blocklocal`."""
+    B, Hq, L, D = q.shape
+    if anchor_len is None:
+        anchor_len = block_b
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq * L):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, L] tensor")
+    dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
+    st = library().star_phase1_rope(
+        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(block_b), int(anchor_len),
+        float(base), float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
+    _lib.check("star_phase1_rope", st)
     return out, lse
 
 

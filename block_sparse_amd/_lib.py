@@ -25,7 +25,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # every symbol include/star_attn.h declares
 EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
-           "star_phase1_prefix", "star_gather_rows", "star_stream_read", "star_pulsar_prefix",
+           "star_phase1_prefix", "star_phase1_rope", "star_gather_rows", "star_stream_read", "star_pulsar_prefix",
            "star_phase2_partial", "star_lse_merge", "star_decode_step",
            "star_context_create", "star_context_destroy", "star_rmsnorm", "star_linear",
            "star_status_string",
@@ -53,6 +53,7 @@ _SIGS = {
     "star_kv_append": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_decode_prepare": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp]),
+    "star_phase1_rope": (ctypes.c_int, [_T, _T, _T, _i64, _i64, ctypes.c_double, _f32, _T, _vp, _vp]),
     "star_phase1_prefix": (ctypes.c_int, [_T, _T, _T, _T, _T, _P(_i64), _P(_i64), _i32, _i64,
                                           _f32, _T, _vp, _vp]),
     "star_gather_rows": (ctypes.c_int, [_T, _vp, _T, _vp]),

@@ -166,7 +166,7 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 201; }
+int star_abi_version(void) { return 202; }
 
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
                     int64_t pos0, double base, void* stream) {
@@ -291,6 +291,28 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const sta
   p.pk_rows = k->S;
   p.a = anchor_len < p.b ? anchor_len : p.b;
   if (block_b >= q->S) p.a = 0;  // a single block has no anchor
+  return hip_status(star::launch_flash(p, (hipStream_t)stream));
+}
+
+int star_phase1_rope(const star_tensor* q, const star_tensor* k, const star_tensor* v,
+                     int64_t block_b, int64_t anchor_len, double base, float scale,
+                     const star_tensor* o, float* lse, void* stream) {
+  int s;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if (anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
+  if (!std::isfinite(base) || !(base > 1.0)) return STAR_ERR_SHAPE;
+  if (q->S == 0) return STAR_OK;
+  star::FlashParams p;
+  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  p.pk = p.k;
+  p.pv = p.v;
+  p.pk_rows = k->S;
+  p.a = anchor_len < p.b ? anchor_len : p.b;
+  if (block_b >= q->S) p.a = 0;  // a single block has no anchor
+  p.q_rope = 1;
+  fill_inv_freq(p.inv_freq, q->D, base);
+  // the rotation lives in the bf16, D = 128 kernel only
+  if (!star::flash2_supported(p)) return STAR_ERR_UNSUPPORTED;
   return hip_status(star::launch_flash(p, (hipStream_t)stream));
 }
 

@@ -39,6 +39,10 @@ struct FlashParams {
   int64_t L, b, a;
   int32_t nblocks, nqt_full, nqt_last, nqt0;
   int32_t prefix_tab;    // 1: range A of block i is pk/pv rows [offs[i], offs[i] + chunk[i])
+  // 1: q holds un-rotated rows; the kernel applies rotate-half RoPE at the
+  // row's position with these inverse frequencies (D = 128) before use
+  int32_t q_rope;
+  double inv_freq[64];
   // Phase 2
   int32_t P, splits, nqt2;
   // Phase 2: partition offsets and split chunk length per partition.

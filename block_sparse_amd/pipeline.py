@@ -32,7 +32,8 @@ import math
 import torch
 
 from . import (decode_prepare, decode_step, gather_rows, kv_append, lse_merge,
-               phase1_blocklocal, phase1_prefix, phase2_partial, pulsar_prefix, rope_apply)
+               phase1_blocklocal, phase1_prefix, phase1_rope, phase2_partial, pulsar_prefix,
+               rope_apply)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -55,7 +56,8 @@ class StarAttentionStep:
 
     def __init__(self, B, Hq, Hkv, D, L, b, Lq, T, anchor=None, rope=True,
                  base=500000.0, device="cuda", want_lse=True,
-                 splits_query=None, splits_decode=None, fused_decode=True):
+                 splits_query=None, splits_decode=None, fused_decode=True,
+                 fuse_q_rope=True):
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
         self.L, self.b, self.Lq, self.T = L, b, Lq, T
         self.a = b if anchor is None else anchor
@@ -88,6 +90,12 @@ class StarAttentionStep:
         self.lp_d = torch.empty((nd, B, Hq, 1), dtype=torch.float32, device=dev)
         # rope + append + partials in one launch per token (star_decode_step)
         self.fused_decode = fused_decode
+        # Phase 1 rotates the context Q itself (star_phase1_rope): no separate
+        # pass over Q; the rotated copy self.qr is made only if a Phase-1
+        # variant needs it
+        self.fuse_q_rope = bool(fuse_q_rope and rope and D == 128)
+        self._qraw = None
+        self._qr_ok = False
 
     # -- inputs -----------------------------------------------------------
     def load_context(self, v):
@@ -97,17 +105,33 @@ class StarAttentionStep:
     # -- phases -----------------------------------------------------------
     def rope_context(self, q, k):
         L = self.L
+        self._qraw, self._qr_ok = q, False
         if self.rope:
-            rope_apply(q, pos0=0, base=self.base, out=self.qr)
+            if not self.fuse_q_rope:
+                rope_apply(q, pos0=0, base=self.base, out=self.qr)
+                self._qr_ok = True
             rope_apply(k, pos0=0, base=self.base, out=self.kc[:, :, :L])
         else:
             self.qr.copy_(q)
+            self._qr_ok = True
             self.kc[:, :, :L].copy_(k)
+
+    def rotated_q(self):
+        """The context Q at its positions (made on first use when Phase 1
+        rotates Q itself)."""
+        if not self._qr_ok:
+            rope_apply(self._qraw, pos0=0, base=self.base, out=self.qr)
+            self._qr_ok = True
+        return self.qr
 
     def phase1(self):
         L = self.L
-        phase1_blocklocal(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
-                          self.scale, out=self.o1, lse=self.lse1)
+        if self.fuse_q_rope:
+            phase1_rope(self._qraw, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
+                        self.base, self.scale, out=self.o1, lse=self.lse1)
+        else:
+            phase1_blocklocal(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
+                              self.scale, out=self.o1, lse=self.lse1)
 
     def pulsar_setup(self, tokens, m: int = 32, sink: int = 64, k: int = 16):
         """Host-side Max-IDF selection for every sequence (``tokens[B, L]``)
@@ -126,13 +150,14 @@ class StarAttentionStep:
         """Phase 1 with Pulsar's prefix: gather the sink and summary rows of
         the rotated cache, then block-local attention over [prefix ; block]."""
         L = self.L
+        qr = self.rotated_q()
         for bb, (rows_d, st, ln, pk, pv) in enumerate(self.pulsar):
             sl = slice(bb, bb + 1)
             if rows_d.numel():
                 gather_rows(self.kc[sl, :, :L], rows_d, out=pk)
                 gather_rows(self.vc[sl, :, :L], rows_d, out=pv)
             lse = None if self.lse1 is None else self.lse1[sl]
-            phase1_prefix(self.qr[sl], self.kc[sl, :, :L], self.vc[sl, :, :L], pk, pv, st, ln,
+            phase1_prefix(qr[sl], self.kc[sl, :, :L], self.vc[sl, :, :L], pk, pv, st, ln,
                           self.b, self.scale, out=self.o1[sl], lse=lse)
 
     def anchor_remap_setup(self, positions):
@@ -156,7 +181,7 @@ class StarAttentionStep:
             rope_apply(k_pre[:, :, :a], pos=self.apos[i], base=self.base,
                        out=self.apk[:, :, i * a:(i + 1) * a])
         gather_rows(self.vc[:, :, :L], self.arows, out=self.apv)
-        phase1_prefix(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.apk, self.apv,
+        phase1_prefix(self.rotated_q(), self.kc[:, :, :L], self.vc[:, :, :L], self.apk, self.apv,
                       self.ast, self.aln, self.b, self.scale, out=self.o1, lse=self.lse1)
 
     def query(self, qq, kq, vq):

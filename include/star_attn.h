@@ -156,6 +156,26 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
                            const star_tensor* o, float* lse, void* stream);
 
 /*
+ * Phase 1 with the RoPE of Q fused in: as star_phase1_blocklocal, but q
+ * holds the un-rotated query rows and the kernel rotates row r at its
+ * original position r (rotate-half, theta_j = base^(-2j/D); Pith review of
+ * Star Attention, "What carries the argument": original position ids), as
+ * star_rope_apply would, before attending.  k must already be rotated (it
+ * is the KV cache).  The angle is reduced modulo 2 pi in fp64 and its
+ * sin/cos come from the hardware approximations (within 4e-7 of exact up
+ * to position 2^20), so a rotated element may differ from
+ * star_rope_apply's by one bf16 rounding step.  Saves the separate pass
+ * over Q and its rotated copy.
+ *   base   > 1.
+ * Returns STAR_ERR_UNSUPPORTED unless q/k/v are bf16 with D = 128 (the
+ * kernel that carries the rotation).
+ */
+int star_phase1_rope(const star_tensor* q, const star_tensor* k,
+                     const star_tensor* v, int64_t block_b,
+                     int64_t anchor_len, double base, float scale,
+                     const star_tensor* o, float* lse, void* stream);
+
+/*
  * Phase 1 with an explicit per-block prefix in place of the anchor.
  * Rows of block i (i = 0 .. nblocks-1, blocks as in
  * star_phase1_blocklocal) attend to every row of

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 201
+    assert lib.star_abi_version() == 202
 
 
 def test_status_strings(lib):
@@ -78,6 +78,28 @@ def test_phase1_validation(lib):
     # empty context: nothing to do, nothing enqueued
     z = dict(B=1, S=0, D=64)
     assert p1(lib, T(H=2, **z), T(H=1, **z), T(H=1, **z), T(H=2, **z)) == 0
+
+
+def test_phase1_rope_validation(lib):
+    """The fused-RoPE Phase 1 shares the Phase-1 checks, requires a finite
+    base above 1 and serves only bf16 with D = 128 (no launch here)."""
+    ok = dict(B=1, H=2, S=64, D=128)
+    q, k, v, o = T(**ok), T(B=1, H=1, S=64, D=128), T(B=1, H=1, S=64, D=128), T(**ok)
+    r = lambda q=q, k=k, v=v, o=o, b=16, a=16, base=500000.0, scale=0.1: lib.star_phase1_rope(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), b, a, base, scale,
+        ctypes.byref(o), None, None)
+    assert lib.star_phase1_rope(None, ctypes.byref(k), ctypes.byref(v), 16, 16, 500000.0, 0.1,
+                                ctypes.byref(o), None, None) == -1
+    assert r(base=1.0) == -2
+    assert r(base=float("nan")) == -2
+    assert r(b=16, a=17) == -2
+    assert r(scale=-1.0) == -2
+    small = dict(B=1, S=64, D=64)
+    assert r(q=T(H=2, **small), k=T(H=1, **small), v=T(H=1, **small), o=T(H=2, **small)) == -5
+    assert r(q=T(**ok, dtype=1), k=T(B=1, H=1, S=64, D=128, dtype=1),
+             v=T(B=1, H=1, S=64, D=128, dtype=1)) == -5            # fp32 inputs
+    z = dict(B=1, S=0, D=128)
+    assert r(q=T(H=2, **z), k=T(H=1, **z), v=T(H=1, **z), o=T(H=2, **z)) == 0
 
 
 def p2(lib, q, kc, vc, offs, P=None, splits=1, qpos=0, scale=0.1, op=FAKE, lp=FAKE):

@@ -50,6 +50,42 @@ def test_phase1_parity(case):
     check_lse(host64(lse), ref_l, "LSE")
 
 
+P1_ROPE_CASES = [
+    # B, Hq, Hkv, L, b, a
+    (2, 8, 2, 700, 200, 200),      # ragged tail, b % 64 != 0
+    (1, 32, 8, 1000, 256, 256),    # Llama-8B heads
+    (1, 8, 1, 333, 1000, 1000),    # one block
+    (1, 16, 16, 130, 64, 0),       # MHA, no anchor
+]
+
+
+@pytest.mark.parametrize("case", P1_ROPE_CASES, ids=[str(i) for i in range(len(P1_ROPE_CASES))])
+def test_phase1_rope_parity(case):
+    """Phase 1 with the RoPE of Q done in the kernel against the oracle
+    (Q rotated exactly in fp64 at positions 0..L-1, rounded to bf16), and
+    against the two-pass GPU path (star_rope_apply, then Phase 1)."""
+    B, Hq, Hkv, L, b, a = case
+    D, base = 128, 500000.0
+    print(f"phase1 rope case {case}", flush=True)
+    q, k, v = _qkv(17, B, Hq, Hkv, L, D, True, 1.0)
+    pos = np.arange(L)
+    k_rot = so.round_bf16(so.rope(f64(k), pos, base))
+    kd = to_dev(k_rot.astype(np.float32)).to(torch.bfloat16)
+    qd, vd = to_dev(q), to_dev(v)
+    scale = 1 / math.sqrt(D)
+    o, lse = sa.phase1_rope(qd, kd, vd, b, a, base, want_lse=True)
+    qr = sa.rope_apply(qd, pos0=0, base=base, out=torch.empty_like(qd))
+    o2, lse2 = sa.phase1_blocklocal(qr, kd, vd, b, a,
+                                    want_lse=True)
+    torch.cuda.synchronize()
+    q_rot = so.round_bf16(so.rope(f64(q), pos, base))
+    ref_o, ref_l = so.phase1(q_rot, k_rot, f64(v), b, a if b < L else 0, scale)
+    check_out(host64(o), ref_o, "O (fused rope)", bf16_out=True)
+    check_lse(host64(lse), ref_l, "LSE (fused rope)")
+    check_out(host64(o2), ref_o, "O (two passes)", bf16_out=True)
+    check_lse(host64(lse2), ref_l, "LSE (two passes)")
+
+
 # (q scale, k scale at position 0, k scale at the last position)
 RESCALE_CASES = [(2.0, 2.0, 8.0), (2.0, 8.0, 2.0), (6.0, 6.0, 6.0)]
 
