@@ -19,7 +19,7 @@ import math
 
 import torch
 
-from . import Context, linear, phase1_blocklocal, rmsnorm, rope_apply
+from . import Context, linear, phase1_blocklocal, phase1_rope, rmsnorm, rope_apply
 
 
 class AttentionLayers:
@@ -71,12 +71,19 @@ class AttentionLayers:
             q = self.heads(self.qkv, 0, self.Hq)
             k = self.heads(self.qkv, self.Hq, self.Hkv)
             v = self.heads(self.qkv, self.Hq + self.Hkv, self.Hkv)
+            # Phase 1 rotates q itself (bf16, D = 128): only k gets its own pass
+            fused = self.rope and self.D == 128
             if self.rope:
-                rope_apply(q, pos0=0, base=self.base)
+                if not fused:
+                    rope_apply(q, pos0=0, base=self.base)
                 rope_apply(k, pos0=0, base=self.base)
             mark("rope")
-            phase1_blocklocal(q, k, v, self.b, self.a, self.scale,
-                              out=self.heads(self.attn, 0, self.Hq))
+            if fused:
+                phase1_rope(q, k, v, self.b, self.a, self.base, self.scale,
+                            out=self.heads(self.attn, 0, self.Hq))
+            else:
+                phase1_blocklocal(q, k, v, self.b, self.a, self.scale,
+                                  out=self.heads(self.attn, 0, self.Hq))
             mark("phase1")
             nxt = self.xs[i % 2]
             linear(self.ctx, self.attn, wo, residual=cur, out=nxt)
