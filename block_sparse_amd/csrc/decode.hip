@@ -20,6 +20,7 @@
 // waves merge their (m, l, O) in LDS at the end.
 #include "common.h"
 #include "internal.h"
+#include "rope_math.h"
 
 #include <type_traits>
 
@@ -119,8 +120,10 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
           for (int e = 0; e < 8; ++e) {
             const float c = p.rc[8 * ch + e], sn = p.rs[8 * ch + e];
             const float a1 = (float)x1[e], a2 = (float)x2[e];
-            y1[e] = (__bf16)(a1 * c - a2 * sn);
-            y2[e] = (__bf16)(a2 * c + a1 * sn);
+            float r1, r2;
+            rope_rotate(a1, a2, c, sn, r1, r2);
+            y1[e] = (__bf16)r1;
+            y2[e] = (__bf16)r2;
           }
         }
         *reinterpret_cast<bf16x8*>(kc + 8 * ch) = y1;
@@ -217,8 +220,10 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
             const int j = 32 * dc + 8 * kg + e;
             const float c = p.rc[j], sn = p.rs[j];
             const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + NDC / 2][e];
-            y1[e] = (__bf16)(x1 * c - x2 * sn);
-            y2[e] = (__bf16)(x2 * c + x1 * sn);
+            float r1, r2;
+            rope_rotate(x1, x2, c, sn, r1, r2);
+            y1[e] = (__bf16)r1;
+            y2[e] = (__bf16)r2;
           }
           qf[dc] = y1;
           qf[dc + NDC / 2] = y2;

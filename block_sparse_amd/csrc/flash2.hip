@@ -41,6 +41,7 @@
 #include "common.h"
 #include "internal.h"
 #include "flash_items.h"
+#include "rope_math.h"
 
 #include <type_traits>
 
@@ -111,30 +112,20 @@ __device__ __forceinline__ s16x4 tr_read(int addr) {
 
 // Rotate-half RoPE of this lane's Q fragments in place, at position pos:
 // the lane holds d = 16 dc + 8 hf + e, and its partner d + 64 sits in
-// fragment dc + 4.  The angle pos * inv_freq is formed and reduced modulo
-// 2 pi in fp64 (two-constant Cody-Waite step), then the hardware sin/cos of
-// the reduced angle (within 4e-7 of the exact values over positions up to
-// 2^20); the rotation is done in fp32 and rounded to bf16, as a stored
-// rotated Q would be.
+// fragment dc + 4.  Angle, sin/cos and rotation are the RoPE kernel's
+// (rope_math.h), then one rounding to bf16, so the rotated Q is bit for bit
+// the one star_rope_apply would store.
 __device__ __forceinline__ void rope_q(bf16x8* qf, double pos, int hf, const double* inv_freq) {
-  constexpr double kTwoPiHi = 6.283185307179586;
-  constexpr double kTwoPiLo = 2.4492935982947064e-16;
-  constexpr double kInvTwoPi = 0.15915494309189535;
 #pragma unroll
   for (int dc = 0; dc < 4; ++dc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 16 * dc + e;
-      const double f = hf ? inv_freq[j + 8] : inv_freq[j];
-      const double ang = pos * f;
-      const double k = rint(ang * kInvTwoPi);
-      double r = fma(-k, kTwoPiHi, ang);
-      r = fma(-k, kTwoPiLo, r);
-      const float rev = (float)r * (float)kInvTwoPi;
-      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-      const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + 4][e];
-      qf[dc][e] = (__bf16)(x1 * cs - x2 * sn);
-      qf[dc + 4][e] = (__bf16)(x2 * cs + x1 * sn);
+      float cs, sn, y1, y2;
+      rope_angle(pos, hf ? inv_freq[j + 8] : inv_freq[j], cs, sn);
+      rope_rotate((float)qf[dc][e], (float)qf[dc + 4][e], cs, sn, y1, y2);
+      qf[dc][e] = (__bf16)y1;
+      qf[dc + 4][e] = (__bf16)y2;
     }
 }
 

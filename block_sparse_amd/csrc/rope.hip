@@ -7,31 +7,17 @@
 // position ids preserve RoPE geometry).  Rotate-half form: pair (j, j+D/2)
 // turns by pos * theta_j.
 //
-// The angle pos * theta_j reaches ~1e6 rad at million-token positions, where
-// an fp32 product is off by up to ~5e-2 rad.  Here it is formed and reduced
-// modulo 2*pi in fp64 (two-constant Cody-Waite step), so the fp32 angle
-// handed to sincosf is within ~1e-7 rad of the exact one.
+// The angle and the rotation are in rope_math.h (fp64 angle reduction).
 //
 // Both kernels are HBM-bound streams: a thread owns 8 pairs of one row
 // (two 16-byte loads for bf16), computes their sin/cos once and applies them
 // to every head of that position, so the trigonometry is amortised over H.
 #include "common.h"
 #include "internal.h"
+#include "rope_math.h"
 
 namespace star {
 namespace {
-
-constexpr double kTwoPiHi = 6.283185307179586;          // fp64(2*pi)
-constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189535;
-
-__device__ __forceinline__ void rope_angle(double pos, double inv_freq, float& c, float& s) {
-  const double ang = pos * inv_freq;
-  const double k = rint(ang * kInvTwoPi);
-  double r = fma(-k, kTwoPiHi, ang);
-  r = fma(-k, kTwoPiLo, r);
-  sincosf((float)r, &s, &c);
-}
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* out);
@@ -102,8 +88,7 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeParams p, int hgrou
       load8<T>(xr + half + 8 * ch, x2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        y1[i] = x1[i] * cs[i] - x2[i] * sn[i];
-        y2[i] = x2[i] * cs[i] + x1[i] * sn[i];
+        rope_rotate(x1[i], x2[i], cs[i], sn[i], y1[i], y2[i]);
       }
       store8<T>(yr + 8 * ch, y1);
       store8<T>(yr + half + 8 * ch, y2);
@@ -143,8 +128,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
       for (int i = 0; i < 8; ++i) {
         float c, s;
         rope_angle(pos, p.inv_freq[8 * ch + i], c, s);
-        y1[i] = x1[i] * c - x2[i] * s;
-        y2[i] = x2[i] * c + x1[i] * s;
+        rope_rotate(x1[i], x2[i], c, s, y1[i], y2[i]);
       }
     } else {
 #pragma unroll
@@ -206,8 +190,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const PrepareParams pp) {
       for (int i = 0; i < 8; ++i) {
         float c, sn;
         rope_angle(pos, p.inv_freq[8 * ch + i], c, sn);
-        y1[i] = x1[i] * c - x2[i] * sn;
-        y2[i] = x2[i] * c + x1[i] * sn;
+        rope_rotate(x1[i], x2[i], c, sn, y1[i], y2[i]);
       }
     } else {
 #pragma unroll

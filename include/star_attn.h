@@ -161,11 +161,10 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
  * original position r (rotate-half, theta_j = base^(-2j/D); Pith review of
  * Star Attention, "What carries the argument": original position ids), as
  * star_rope_apply would, before attending.  k must already be rotated (it
- * is the KV cache).  The angle is reduced modulo 2 pi in fp64 and its
- * sin/cos come from the hardware approximations (within 4e-7 of exact up
- * to position 2^20), so a rotated element may differ from
- * star_rope_apply's by one bf16 rounding step.  Saves the separate pass
- * over Q and its rotated copy.
+ * is the KV cache).  The rotation is star_rope_apply's (same fp64 angle
+ * reduction, sin/cos and rounding), so the output equals that of
+ * star_rope_apply followed by star_phase1_blocklocal bit for bit.  Saves
+ * the separate pass over Q and its rotated copy.
  *   base   > 1.
  * Returns STAR_ERR_UNSUPPORTED unless q/k/v are bf16 with D = 128 (the
  * kernel that carries the rotation).

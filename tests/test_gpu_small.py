@@ -63,7 +63,8 @@ P1_ROPE_CASES = [
 def test_phase1_rope_parity(case):
     """Phase 1 with the RoPE of Q done in the kernel against the oracle
     (Q rotated exactly in fp64 at positions 0..L-1, rounded to bf16), and
-    against the two-pass GPU path (star_rope_apply, then Phase 1)."""
+    against the two-pass GPU path (star_rope_apply, then Phase 1), which it
+    must equal bit for bit."""
     B, Hq, Hkv, L, b, a = case
     D, base = 128, 500000.0
     print(f"phase1 rope case {case}", flush=True)
@@ -84,6 +85,8 @@ def test_phase1_rope_parity(case):
     check_lse(host64(lse), ref_l, "LSE (fused rope)")
     check_out(host64(o2), ref_o, "O (two passes)", bf16_out=True)
     check_lse(host64(lse2), ref_l, "LSE (two passes)")
+    # the in-kernel rotation is the RoPE kernel's, bit for bit
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
 # (q scale, k scale at position 0, k scale at the last position)
