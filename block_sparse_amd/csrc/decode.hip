@@ -42,6 +42,7 @@ __device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
 #if __HIP_DEVICE_COMPILE__
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 #else
+  (void)p;
   return s16x4{0, 0, 0, 0};
 #endif
 }
