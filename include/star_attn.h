@@ -32,7 +32,10 @@
  *   passed by the caller, normally 1/sqrt(D)).  A row that sees no key has
  *   o = 0 and lse = -inf.
  * - Ownership: the caller allocates and owns every buffer.  No entry point
- *   allocates, frees or synchronises.  Work is enqueued on `stream` (a
+ *   allocates, frees or synchronises, with two exceptions in the attention
+ *   layer's calls: star_context_create allocates the context, and
+ *   star_linear runs rocBLAS, which manages its own device workspace (it
+ *   may allocate it on a first call).  Work is enqueued on `stream` (a
  *   hipStream_t passed as void*; NULL = the null stream) and the call returns
  *   without waiting.  The library holds no mutable global state, so calls
  *   are reentrant and thread-safe.
