@@ -22,7 +22,7 @@ from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
 __all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
-           "phase1_prefix",
+           "phase1_prefix", "sched_workspace", "SCHED_INTS",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
            "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
            "StarError", "library"]
@@ -56,6 +56,30 @@ def _stream(t: torch.Tensor):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# int32 count of a Phase-1 scheduling workspace (STAR_SCHED_INTS)
+SCHED_INTS = 16
+
+
+def sched_workspace(device=None) -> torch.Tensor:
+    """A Phase-1 scheduling workspace: ``SCHED_INTS`` int32 on ``device``.
+    Passed as ``sched=`` to the Phase-1 calls, it lets the kernel hand out
+    its items from per-XCD queues (faster XCDs take over the slower ones'
+    remaining items); results are identical with or without it.  One
+    workspace must not serve two calls that may run at the same time."""
+    return torch.zeros(SCHED_INTS, dtype=torch.int32, device=device)
+
+
+def _sched_ptr(sched, like: torch.Tensor):
+    if sched is None:
+        return None
+    if (not isinstance(sched, torch.Tensor) or sched.dtype != torch.int32
+            or sched.numel() < SCHED_INTS or not sched.is_contiguous()
+            or sched.device != like.device):
+        raise ValueError(f"sched must be a contiguous int32 tensor of at least {SCHED_INTS} "
+                         "elements on the inputs' device")
+    return ctypes.c_void_p(sched.data_ptr())
 
 
 def rope_apply(x: torch.Tensor, pos: torch.Tensor | None = None, pos0: int = 0,
@@ -95,9 +119,10 @@ def decode_prepare(q_new, q_out, k_new, v_new, k_cache, v_cache, slot0: int, pos
 
 def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,
                       scale: float | None = None, out=None, lse=None,
-                      want_lse: bool = False):
+                      want_lse: bool = False, sched=None):
     """Phase 1 context encoding.  Returns ``(o, lse)`` (lse None unless
-    ``want_lse`` or an ``lse`` buffer is given)."""
+    ``want_lse`` or an ``lse`` buffer is given).  ``sched``: optional
+    scheduling workspace (:func:`sched_workspace`)."""
     B, Hq, L, D = q.shape
     if anchor_len is None:
         anchor_len = block_b
@@ -113,14 +138,14 @@ def phase1_blocklocal(q, k, v, block_b: int, anchor_len: int | None = None,
     dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
     st = library().star_phase1_blocklocal(
         ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(block_b), int(anchor_len),
-        float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
+        float(scale), ctypes.byref(do), _ptr(lse), _sched_ptr(sched, q), _stream(q))
     _lib.check("star_phase1_blocklocal", st)
     return out, lse
 
 
 def phase1_rope(q, k, v, block_b: int, anchor_len: int | None = None,
                 base: float = 500000.0, scale: float | None = None, out=None, lse=None,
-                want_lse: bool = False):
+                want_lse: bool = False, sched=None):
     """Phase 1 with the RoPE of ``q`` fused in: ``q`` holds un-rotated rows
     (rotated in the kernel at positions 0..L-1), ``k`` is already rotated.
     bf16, D = 128.  Returns ``(o, lse)`` like :func:`phase1_blocklocal`."""
@@ -139,13 +164,14 @@ def phase1_rope(q, k, v, block_b: int, anchor_len: int | None = None,
     dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
     st = library().star_phase1_rope(
         ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(block_b), int(anchor_len),
-        float(base), float(scale), ctypes.byref(do), _ptr(lse), _stream(q))
+        float(base), float(scale), ctypes.byref(do), _ptr(lse), _sched_ptr(sched, q), _stream(q))
     _lib.check("star_phase1_rope", st)
     return out, lse
 
 
 def phase1_prefix(q, k, v, pk, pv, prefix_start, prefix_len, block_b: int,
-                  scale: float | None = None, out=None, lse=None, want_lse: bool = False):
+                  scale: float | None = None, out=None, lse=None, want_lse: bool = False,
+                  sched=None):
     """Phase 1 where block i attends to all of ``pk/pv`` rows
     ``[prefix_start[i], prefix_start[i] + prefix_len[i])`` and then causally
     within itself.  ``prefix_start``/``prefix_len`` are host sequences of
@@ -169,7 +195,7 @@ def phase1_prefix(q, k, v, pk, pv, prefix_start, prefix_len, block_b: int,
     do = _desc(out)
     st = library().star_phase1_prefix(*[ctypes.byref(x) for x in d], st_arr, ln_arr, int(n),
                                       int(block_b), float(scale), ctypes.byref(do), _ptr(lse),
-                                      _stream(q))
+                                      _sched_ptr(sched, q), _stream(q))
     _lib.check("star_phase1_prefix", st)
     return out, lse
 

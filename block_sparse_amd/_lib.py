@@ -52,10 +52,11 @@ _SIGS = {
     "star_rope_apply": (ctypes.c_int, [_T, _T, _vp, _i64, _f64, _vp]),
     "star_kv_append": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_decode_prepare": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
-    "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp]),
-    "star_phase1_rope": (ctypes.c_int, [_T, _T, _T, _i64, _i64, ctypes.c_double, _f32, _T, _vp, _vp]),
+    "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp, _vp]),
+    "star_phase1_rope": (ctypes.c_int, [_T, _T, _T, _i64, _i64, ctypes.c_double, _f32, _T, _vp,
+                                        _vp, _vp]),
     "star_phase1_prefix": (ctypes.c_int, [_T, _T, _T, _T, _T, _P(_i64), _P(_i64), _i32, _i64,
-                                          _f32, _T, _vp, _vp]),
+                                          _f32, _T, _vp, _vp, _vp]),
     "star_gather_rows": (ctypes.c_int, [_T, _vp, _T, _vp]),
     "star_stream_read": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
     "star_pulsar_prefix": (ctypes.c_int, [_P(_i32), _i64, _i64, _i32, _i32, _i32, _P(_i64), _i64,

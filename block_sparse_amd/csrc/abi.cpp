@@ -104,9 +104,10 @@ void decode_params(star::DecodeParams& p, const star_tensor* q, const star_tenso
   p.lse = lse_part;
 }
 
-// Validation shared by the two Phase-1 entry points.
+// Validation shared by the Phase-1 entry points.
 int check_phase1(const star_tensor* q, const star_tensor* k, const star_tensor* v,
-                 int64_t block_b, float scale, const star_tensor* o, const float* lse) {
+                 int64_t block_b, float scale, const star_tensor* o, const float* lse,
+                 const int32_t* sched) {
   int s;
   if ((s = check_qkv(q, k, v)) != STAR_OK) return s;
   if ((s = check_tensor(o, false)) != STAR_OK) return s;
@@ -115,6 +116,7 @@ int check_phase1(const star_tensor* q, const star_tensor* k, const star_tensor* 
   if (block_b < 1) return STAR_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  if (sched != nullptr && (reinterpret_cast<uintptr_t>(sched) & 3u)) return STAR_ERR_ALIGN;
   return STAR_OK;
 }
 
@@ -122,7 +124,7 @@ int check_phase1(const star_tensor* q, const star_tensor* k, const star_tensor* 
 // filled by the caller).
 void phase1_params(star::FlashParams& p, const star_tensor* q, const star_tensor* k,
                    const star_tensor* v, int64_t block_b, float scale, const star_tensor* o,
-                   float* lse) {
+                   float* lse, int32_t* sched) {
   std::memset(&p, 0, sizeof(p));
   p.q = ref(q);
   p.k = ref(k);
@@ -146,6 +148,7 @@ void phase1_params(star::FlashParams& p, const star_tensor* q, const star_tensor
   p.osH = o->sH;
   p.osS = o->sS;
   p.lse = lse;
+  p.sched = sched;
 }
 
 }  // namespace
@@ -166,7 +169,7 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 202; }
+int star_abi_version(void) { return 300; }
 
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
                     int64_t pos0, double base, void* stream) {
@@ -279,13 +282,13 @@ int star_decode_prepare(const star_tensor* q_new, const star_tensor* q_out,
 
 int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const star_tensor* v,
                            int64_t block_b, int64_t anchor_len, float scale,
-                           const star_tensor* o, float* lse, void* stream) {
+                           const star_tensor* o, float* lse, int32_t* sched, void* stream) {
   int s;
-  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse, sched)) != STAR_OK) return s;
   if (anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
   if (q->S == 0) return STAR_OK;
   star::FlashParams p;
-  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  phase1_params(p, q, k, v, block_b, scale, o, lse, sched);
   p.pk = p.k;
   p.pv = p.v;
   p.pk_rows = k->S;
@@ -296,14 +299,14 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k, const sta
 
 int star_phase1_rope(const star_tensor* q, const star_tensor* k, const star_tensor* v,
                      int64_t block_b, int64_t anchor_len, double base, float scale,
-                     const star_tensor* o, float* lse, void* stream) {
+                     const star_tensor* o, float* lse, int32_t* sched, void* stream) {
   int s;
-  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse, sched)) != STAR_OK) return s;
   if (anchor_len < 0 || anchor_len > block_b) return STAR_ERR_SHAPE;
   if (!std::isfinite(base) || !(base > 1.0)) return STAR_ERR_SHAPE;
   if (q->S == 0) return STAR_OK;
   star::FlashParams p;
-  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  phase1_params(p, q, k, v, block_b, scale, o, lse, sched);
   p.pk = p.k;
   p.pv = p.v;
   p.pk_rows = k->S;
@@ -320,9 +323,9 @@ int star_phase1_prefix(const star_tensor* q, const star_tensor* k, const star_te
                        const star_tensor* pk, const star_tensor* pv,
                        const int64_t* prefix_start, const int64_t* prefix_len, int32_t nblocks,
                        int64_t block_b, float scale, const star_tensor* o, float* lse,
-                       void* stream) {
+                       int32_t* sched, void* stream) {
   int s;
-  if ((s = check_phase1(q, k, v, block_b, scale, o, lse)) != STAR_OK) return s;
+  if ((s = check_phase1(q, k, v, block_b, scale, o, lse, sched)) != STAR_OK) return s;
   if ((s = check_tensor(pk, true)) != STAR_OK) return s;
   if ((s = check_tensor(pv, true)) != STAR_OK) return s;
   if (pk->dtype != q->dtype || pv->dtype != q->dtype) return STAR_ERR_DTYPE;
@@ -338,7 +341,7 @@ int star_phase1_prefix(const star_tensor* q, const star_tensor* k, const star_te
   }
   if (q->S == 0) return STAR_OK;
   star::FlashParams p;
-  phase1_params(p, q, k, v, block_b, scale, o, lse);
+  phase1_params(p, q, k, v, block_b, scale, o, lse, sched);
   p.pk = ref(pk);
   p.pv = ref(pv);
   p.pk_rows = pk->S;

@@ -137,6 +137,43 @@ __device__ __forceinline__ void rope_q(bf16x8* qf, double pos, int hf, const dou
     }
 }
 
+// Dynamic item order (when the caller passes a scheduling workspace).  The
+// items are cut into 8 queues, queue x being the contiguous range the static
+// order gives XCD x (heavy first), and sched[x] counts the tickets handed out
+// from it.  A workgroup takes the next ticket of its own XCD's queue; once
+// that queue is empty it takes one from another queue, so XCDs that run
+// faster (their clocks differ by several percent under this load) take over
+// the slower ones' remaining items.  Items are independent, so the order
+// changes no result; only relaxed atomics are needed.  Returns -1 when every
+// queue is empty (the grid holds more workgroups than items).
+__device__ __forceinline__ int sched_grab(const FlashParams& p) {
+  const int n = p.total_items, base = n >> 3, extra = n & 7;
+  // XCC_ID hardware register (hwreg 20, bits 3:0): this XCD's index
+  const int xcd = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;
+  auto first = [&](int x) { return x * base + (x < extra ? x : extra); };
+  auto count = [&](int x) { return base + (x < extra ? 1 : 0); };
+  if (count(xcd) > 0) {
+    const int t = atomicAdd(p.sched + xcd, 1);
+    if (t < count(xcd)) return first(xcd) + t;
+  }
+  // own queue empty: read every counter once and take from a non-empty one
+  int seen[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+    seen[x] = __hip_atomic_load(p.sched + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int v = 1; v < 8; ++v) {
+    const int x = (xcd + v) & 7;
+    if (seen[x] >= count(x)) continue;
+    const int t = atomicAdd(p.sched + x, 1);
+    if (t < count(x)) return first(x) + t;
+  }
+  return -1;
+}
+
+__global__ void sched_reset_kernel(int32_t* sched) {
+  if (threadIdx.x < STAR_SCHED_INTS) sched[threadIdx.x] = 0;
+}
+
 __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // tile buffer b: K rows at smK + b TILE, V rows at smV + b TILE
   __shared__ __attribute__((aligned(1024))) uint8_t smK[NBUF * TILE];
@@ -148,8 +185,18 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
+  int lid;
+  if (p.sched != nullptr) {
+    __shared__ int s_item;
+    if (tid == 0) s_item = sched_grab(p);
+    __syncthreads();
+    lid = __builtin_amdgcn_readfirstlane(s_item);
+    if (lid < 0) return;
+  } else {
+    lid = xcd_remap(blockIdx.x, p.total_items);
+  }
   Item it;
-  flash_get_item(p, xcd_remap(blockIdx.x, p.total_items), it);
+  flash_get_item(p, lid, it);
 
   const int64_t qlast = min(it.qr0 + p.m_pos, it.qr_end) - 1;
   const int64_t pmax = qlast + p.pos_shift;
@@ -522,7 +569,16 @@ bool flash2_supported(const FlashParams& p) {
 hipError_t launch_flash2(FlashParams& p, hipStream_t stream) {
   if (!flash_geometry(p, NW)) return hipErrorInvalidValue;
   if (p.total_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(flash2_kernel, dim3(p.total_items), dim3(NW * 64), 0, stream, p);
+  int grid = p.total_items;
+  if (p.sched != nullptr) {
+    // one eighth more workgroups than items: the spare ones serve the XCDs
+    // that empty their own queue first, the rest find nothing and exit
+    const int spare = ((p.total_items / 8 + 7) / 8) * 8 + 8;
+    if (p.total_items > 0x7fffffff - spare) return hipErrorInvalidValue;
+    grid += spare;
+    hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.sched);
+  }
+  hipLaunchKernelGGL(flash2_kernel, dim3(grid), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

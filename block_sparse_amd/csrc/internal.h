@@ -54,6 +54,9 @@ struct FlashParams {
   int64_t osB, osH, osS;
   float* lse;            // Phase 1 lse (nullable) or Phase-2 lse_part
   float* opart;          // Phase-2 o_part
+  // scheduling workspace (STAR_SCHED_INTS int32, device) or NULL: with it
+  // the bf16 D = 128 kernel takes its items from per-XCD queues
+  int32_t* sched;
 };
 
 hipError_t launch_flash(FlashParams& p, hipStream_t stream);

@@ -19,7 +19,8 @@ import math
 
 import torch
 
-from . import Context, linear, phase1_blocklocal, phase1_rope, rmsnorm, rope_apply
+from . import (Context, linear, phase1_blocklocal, phase1_rope, rmsnorm, rope_apply,
+               sched_workspace)
 
 
 class AttentionLayers:
@@ -49,6 +50,7 @@ class AttentionLayers:
         self.qkv = torch.empty((M, self.N), dtype=bf, device=dev)
         self.attn = torch.empty((M, Hq * D), dtype=bf, device=dev)
         self.xs = [torch.empty((M, H), dtype=bf, device=dev) for _ in range(2)]
+        self.sched = sched_workspace(dev)   # Phase-1 work queues (one stream)
 
     def heads(self, t, first, n):
         """[B, n, L, D] view of heads first..first+n-1 of a [B*L, cols] buffer."""
@@ -80,10 +82,10 @@ class AttentionLayers:
             mark("rope")
             if fused:
                 phase1_rope(q, k, v, self.b, self.a, self.base, self.scale,
-                            out=self.heads(self.attn, 0, self.Hq))
+                            out=self.heads(self.attn, 0, self.Hq), sched=self.sched)
             else:
                 phase1_blocklocal(q, k, v, self.b, self.a, self.scale,
-                                  out=self.heads(self.attn, 0, self.Hq))
+                                  out=self.heads(self.attn, 0, self.Hq), sched=self.sched)
             mark("phase1")
             nxt = self.xs[i % 2]
             linear(self.ctx, self.attn, wo, residual=cur, out=nxt)

@@ -33,7 +33,7 @@ import torch
 
 from . import (decode_prepare, decode_step, gather_rows, kv_append, lse_merge,
                phase1_blocklocal, phase1_prefix, phase1_rope, phase2_partial, pulsar_prefix,
-               rope_apply)
+               rope_apply, sched_workspace)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -57,7 +57,7 @@ class StarAttentionStep:
     def __init__(self, B, Hq, Hkv, D, L, b, Lq, T, anchor=None, rope=True,
                  base=500000.0, device="cuda", want_lse=True,
                  splits_query=None, splits_decode=None, fused_decode=True,
-                 fuse_q_rope=True):
+                 fuse_q_rope=True, dynamic_schedule=True):
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
         self.L, self.b, self.Lq, self.T = L, b, Lq, T
         self.a = b if anchor is None else anchor
@@ -94,6 +94,9 @@ class StarAttentionStep:
         # pass over Q; the rotated copy self.qr is made only if a Phase-1
         # variant needs it
         self.fuse_q_rope = bool(fuse_q_rope and rope and D == 128)
+        # Phase-1 work items from per-XCD queues (the calls of one step run
+        # in order on one stream, so one workspace serves them all)
+        self.sched = sched_workspace(dev) if dynamic_schedule else None
         self._qraw = None
         self._qr_ok = False
 
@@ -128,10 +131,10 @@ class StarAttentionStep:
         L = self.L
         if self.fuse_q_rope:
             phase1_rope(self._qraw, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
-                        self.base, self.scale, out=self.o1, lse=self.lse1)
+                        self.base, self.scale, out=self.o1, lse=self.lse1, sched=self.sched)
         else:
             phase1_blocklocal(self.qr, self.kc[:, :, :L], self.vc[:, :, :L], self.b, self.a,
-                              self.scale, out=self.o1, lse=self.lse1)
+                              self.scale, out=self.o1, lse=self.lse1, sched=self.sched)
 
     def pulsar_setup(self, tokens, m: int = 32, sink: int = 64, k: int = 16):
         """Host-side Max-IDF selection for every sequence (``tokens[B, L]``)
@@ -158,7 +161,7 @@ class StarAttentionStep:
                 gather_rows(self.vc[sl, :, :L], rows_d, out=pv)
             lse = None if self.lse1 is None else self.lse1[sl]
             phase1_prefix(qr[sl], self.kc[sl, :, :L], self.vc[sl, :, :L], pk, pv, st, ln,
-                          self.b, self.scale, out=self.o1[sl], lse=lse)
+                          self.b, self.scale, out=self.o1[sl], lse=lse, sched=self.sched)
 
     def anchor_remap_setup(self, positions):
         """Buffers for the anchor at other position ids: ``positions[i]``
@@ -182,7 +185,8 @@ class StarAttentionStep:
                        out=self.apk[:, :, i * a:(i + 1) * a])
         gather_rows(self.vc[:, :, :L], self.arows, out=self.apv)
         phase1_prefix(self.rotated_q(), self.kc[:, :, :L], self.vc[:, :, :L], self.apk, self.apv,
-                      self.ast, self.aln, self.b, self.scale, out=self.o1, lse=self.lse1)
+                      self.ast, self.aln, self.b, self.scale, out=self.o1, lse=self.lse1,
+                      sched=self.sched)
 
     def query(self, qq, kq, vq):
         L, Lq = self.L, self.Lq

@@ -81,6 +81,20 @@ typedef struct {
 #define STAR_MAX_PARTS 128
 /* Split chunks of a partition are whole multiples of this many keys. */
 #define STAR_SPLIT_ALIGN 64
+/*
+ * Phase-1 scheduling workspace: int32 count of the optional `sched` buffer
+ * of the Phase-1 calls (device memory, 4-byte aligned, owned by the
+ * caller).  With it, the bf16 D = 128 kernel hands out its work items from
+ * per-XCD queues kept in that buffer: an XCD that runs faster than the
+ * others (their clocks differ by several percent under a full load) takes
+ * over their remaining items instead of idling at the end.  NULL keeps a
+ * fixed share per XCD.  Results are identical either way (items are
+ * independent).  The call clears the buffer itself, on `stream`, before
+ * its kernel uses it; the contents are scratch afterwards.  Two calls that
+ * may run at the same time (different streams) must not share a buffer.
+ * The other Phase-1 kernels (D = 64, fp32 inputs) ignore it.
+ */
+#define STAR_SCHED_INTS 16
 
 /*
  * Rotary position embedding at original position ids (rotate-half form).
@@ -152,11 +166,14 @@ int star_decode_prepare(const star_tensor* q_new, const star_tensor* q_out,
  *   k, v   [B, Hkv, L, D], same dtype as q, k rotated.
  *   o      [B, Hq, L, D] bf16 output.
  *   lse    fp32 [B, Hq, L] contiguous output, or NULL.
+ *   sched  device int32 [STAR_SCHED_INTS] scheduling workspace, or NULL
+ *          (see STAR_SCHED_INTS); STAR_ERR_ALIGN unless 4-byte aligned.
  */
 int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
                            const star_tensor* v, int64_t block_b,
                            int64_t anchor_len, float scale,
-                           const star_tensor* o, float* lse, void* stream);
+                           const star_tensor* o, float* lse, int32_t* sched,
+                           void* stream);
 
 /*
  * Phase 1 with the RoPE of Q fused in: as star_phase1_blocklocal, but q
@@ -170,12 +187,13 @@ int star_phase1_blocklocal(const star_tensor* q, const star_tensor* k,
  * the separate pass over Q and its rotated copy.
  *   base   > 1.
  * Returns STAR_ERR_UNSUPPORTED unless q/k/v are bf16 with D = 128 (the
- * kernel that carries the rotation).
+ * kernel that carries the rotation).  sched as for star_phase1_blocklocal.
  */
 int star_phase1_rope(const star_tensor* q, const star_tensor* k,
                      const star_tensor* v, int64_t block_b,
                      int64_t anchor_len, double base, float scale,
-                     const star_tensor* o, float* lse, void* stream);
+                     const star_tensor* o, float* lse, int32_t* sched,
+                     void* stream);
 
 /*
  * Phase 1 with an explicit per-block prefix in place of the anchor.
@@ -201,14 +219,14 @@ int star_phase1_rope(const star_tensor* q, const star_tensor* k,
  *   prefix_start   host int64 [nblocks], prefix_len host int64 [nblocks]:
  *                  0 <= start, 0 <= len, start + len <= R.
  *   nblocks        must equal ceil(L / block_b), at most STAR_MAX_PARTS.
- *   o, lse         as for star_phase1_blocklocal.
+ *   o, lse, sched  as for star_phase1_blocklocal.
  */
 int star_phase1_prefix(const star_tensor* q, const star_tensor* k,
                        const star_tensor* v, const star_tensor* pk,
                        const star_tensor* pv, const int64_t* prefix_start,
                        const int64_t* prefix_len, int32_t nblocks,
                        int64_t block_b, float scale, const star_tensor* o,
-                       float* lse, void* stream);
+                       float* lse, int32_t* sched, void* stream);
 
 /*
  * Row gather: dst[b, h, r, :] = src[b, h, rows[r], :] for r < dst->S.  A

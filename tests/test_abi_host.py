@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 202
+    assert lib.star_abi_version() == 300
 
 
 def test_status_strings(lib):
@@ -48,16 +48,16 @@ def test_status_strings(lib):
     assert b"unknown" in lib.star_status_string(-99)
 
 
-def p1(lib, q, k, v, o, b=16, a=16, scale=0.125, lse=None):
+def p1(lib, q, k, v, o, b=16, a=16, scale=0.125, lse=None, sched=None):
     return lib.star_phase1_blocklocal(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), b, a,
-                                      scale, ctypes.byref(o), lse, None)
+                                      scale, ctypes.byref(o), lse, sched, None)
 
 
 def test_phase1_validation(lib):
     ok = dict(B=1, H=2, S=64, D=64)
     q, k, v, o = T(**ok), T(B=1, H=1, S=64, D=64), T(B=1, H=1, S=64, D=64), T(**ok)
     assert lib.star_phase1_blocklocal(None, ctypes.byref(k), ctypes.byref(v), 16, 16, 0.1,
-                                      ctypes.byref(o), None, None) == -1
+                                      ctypes.byref(o), None, None, None) == -1
     assert p1(lib, T(**ok, data=0), k, v, o) == -1
     assert p1(lib, T(**ok, dtype=7), k, v, o) == -3
     assert p1(lib, q, k, v, T(**ok, dtype=1)) == -3            # O must be bf16
@@ -75,6 +75,7 @@ def test_phase1_validation(lib):
     assert p1(lib, q, T(B=1, H=1, S=63, D=64), T(B=1, H=1, S=63, D=64), o) == -2
     assert p1(lib, q, k, v, T(B=1, H=2, S=32, D=64)) == -2
     assert p1(lib, q, k, v, o, lse=ctypes.c_void_p(FAKE + 1)) == -4
+    assert p1(lib, q, k, v, o, sched=ctypes.c_void_p(FAKE + 2)) == -4   # int32 workspace
     # empty context: nothing to do, nothing enqueued
     z = dict(B=1, S=0, D=64)
     assert p1(lib, T(H=2, **z), T(H=1, **z), T(H=1, **z), T(H=2, **z)) == 0
@@ -87,9 +88,12 @@ def test_phase1_rope_validation(lib):
     q, k, v, o = T(**ok), T(B=1, H=1, S=64, D=128), T(B=1, H=1, S=64, D=128), T(**ok)
     r = lambda q=q, k=k, v=v, o=o, b=16, a=16, base=500000.0, scale=0.1: lib.star_phase1_rope(
         ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), b, a, base, scale,
-        ctypes.byref(o), None, None)
+        ctypes.byref(o), None, None, None)
     assert lib.star_phase1_rope(None, ctypes.byref(k), ctypes.byref(v), 16, 16, 500000.0, 0.1,
-                                ctypes.byref(o), None, None) == -1
+                                ctypes.byref(o), None, None, None) == -1
+    assert lib.star_phase1_rope(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 16, 16,
+                                500000.0, 0.1, ctypes.byref(o), None, ctypes.c_void_p(FAKE + 1),
+                                None) == -4
     assert r(base=1.0) == -2
     assert r(base=float("nan")) == -2
     assert r(b=16, a=17) == -2
@@ -168,13 +172,13 @@ def test_phase1_prefix_validation(lib):
     k, v = T(B=1, H=1, S=64, D=64), T(B=1, H=1, S=64, D=64)
     pk, pv = T(B=1, H=1, S=10, D=64), T(B=1, H=1, S=10, D=64)
 
-    def pp(pk=pk, pv=pv, st=(0, 0, 0, 0), ln=(0, 5, 5, 10), n=None, b=16, q=q):
+    def pp(pk=pk, pv=pv, st=(0, 0, 0, 0), ln=(0, 5, 5, 10), n=None, b=16, q=q, sched=None):
         n = len(st) if n is None else n
         sa = (ctypes.c_int64 * len(st))(*st)
         la = (ctypes.c_int64 * len(ln))(*ln)
         return lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                                       ctypes.byref(pk), ctypes.byref(pv), sa, la, n, b, 0.1,
-                                      ctypes.byref(o), None, None)
+                                      ctypes.byref(o), None, sched, None)
     assert pp(ln=(0, 5, 5, 11)) == -2                  # past the prefix rows
     assert pp(st=(0, 0, 6, 0)) == -2                   # 6 + 5 > 10
     assert pp(st=(0, -1, 0, 0)) == -2
@@ -184,16 +188,17 @@ def test_phase1_prefix_validation(lib):
     assert pp(pv=T(B=1, H=1, S=11, D=64)) == -2        # pk/pv rows differ
     assert pp(pk=T(B=1, H=2, S=10, D=64), pv=T(B=1, H=2, S=10, D=64)) == -2
     assert pp(pk=T(B=1, H=1, S=10, D=64, data=FAKE + 8)) == -4
+    assert pp(sched=ctypes.c_void_p(FAKE + 3)) == -4
     st = [0] * 129
     assert pp(st=st, ln=st, b=1, q=T(B=1, H=2, S=129, D=64)) == -2   # k has 64 rows
     assert lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                                   ctypes.byref(pk), ctypes.byref(pv), None, None, 4, 16, 0.1,
-                                  ctypes.byref(o), None, None) == -1
+                                  ctypes.byref(o), None, None, None) == -1
     z = dict(B=1, S=0, D=64)
     assert lib.star_phase1_prefix(ctypes.byref(T(H=2, **z)), ctypes.byref(T(H=1, **z)),
                                   ctypes.byref(T(H=1, **z)), ctypes.byref(pk), ctypes.byref(pv),
                                   None, None, 0, 16, 0.1, ctypes.byref(T(H=2, **z)), None,
-                                  None) == 0
+                                  None, None) == 0
 
 
 def test_phase1_prefix_too_many_blocks(lib):
@@ -203,7 +208,7 @@ def test_phase1_prefix_too_many_blocks(lib):
     z = (ctypes.c_int64 * 129)(*([0] * 129))
     assert lib.star_phase1_prefix(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                                   ctypes.byref(k), ctypes.byref(v), z, z, 129, b, 0.1,
-                                  ctypes.byref(o), None, None) == -5
+                                  ctypes.byref(o), None, None, None) == -5
 
 
 def test_gather_validation(lib):

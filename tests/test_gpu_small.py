@@ -89,6 +89,56 @@ def test_phase1_rope_parity(case):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+SCHED_CASES = [
+    # B, Hq, Hkv, D, L, b, a, bf16
+    (1, 32, 8, 128, 8192, 1024, 1024, True),   # 1024 items: queues drain and steal
+    (2, 8, 2, 128, 700, 200, 200, True),       # ragged tail
+    (1, 8, 1, 128, 100, 64, 64, True),         # 2 items: most queues empty
+    (1, 4, 4, 64, 600, 256, 100, True),        # D = 64 kernel (ignores sched)
+    (1, 2, 1, 64, 512, 128, 128, False),       # fp32 inputs (ignores sched)
+]
+
+
+@pytest.mark.parametrize("case", SCHED_CASES, ids=[str(i) for i in range(len(SCHED_CASES))])
+def test_phase1_sched_identical(case):
+    """With a scheduling workspace the items are handed out from per-XCD
+    queues instead of a fixed order; the items are independent, so O and lse
+    must be bit for bit those of the fixed order.  The workspace starts with
+    junk (the call clears it itself) and is reused by back-to-back calls of
+    all three Phase-1 entry points."""
+    B, Hq, Hkv, D, L, b, a, bf16 = case
+    print(f"phase1 sched case {case}", flush=True)
+    q, k, v = (to_dev(t) for t in _qkv(23, B, Hq, Hkv, L, D, bf16, 1.0))
+    sched = torch.full((sa.SCHED_INTS,), 12345, dtype=torch.int32, device=q.device)
+    sched[::3] = -7
+    o0, l0 = sa.phase1_blocklocal(q, k, v, b, a, want_lse=True)
+    for rep in range(3):
+        o1, l1 = sa.phase1_blocklocal(q, k, v, b, a, want_lse=True, sched=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), f"blocklocal, call {rep}"
+    n = -(-L // b)
+    st, ln = [0] * n, [0] + [min(a, L)] * (n - 1)
+    p0, pl0 = sa.phase1_prefix(q, k, v, k, v, st, ln, b, want_lse=True)
+    p1, pl1 = sa.phase1_prefix(q, k, v, k, v, st, ln, b, want_lse=True, sched=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(p0, p1) and torch.equal(pl0, pl1), "prefix"
+    if D == 128 and bf16:
+        r0, rl0 = sa.phase1_rope(q, k, v, b, a, want_lse=True)
+        r1, rl1 = sa.phase1_rope(q, k, v, b, a, want_lse=True, sched=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(r0, r1) and torch.equal(rl0, rl1), "rope"
+
+
+def test_phase1_sched_argument_checks():
+    q, k, v = (to_dev(t) for t in _qkv(5, 1, 2, 1, 64, 128, True, 1.0))
+    for bad in (torch.zeros(sa.SCHED_INTS, dtype=torch.int64, device=q.device),
+                torch.zeros(sa.SCHED_INTS - 1, dtype=torch.int32, device=q.device),
+                torch.zeros(sa.SCHED_INTS),
+                torch.zeros(2 * sa.SCHED_INTS, dtype=torch.int32, device=q.device)[::2]):
+        with pytest.raises(ValueError):
+            sa.phase1_blocklocal(q, k, v, 16, 16, sched=bad)
+
+
 # (q scale, k scale at position 0, k scale at the last position)
 RESCALE_CASES = [(2.0, 2.0, 8.0), (2.0, 8.0, 2.0), (6.0, 6.0, 6.0)]
 
