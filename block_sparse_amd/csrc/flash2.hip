@@ -174,6 +174,26 @@ __global__ void sched_reset_kernel(int32_t* sched) {
   if (threadIdx.x < STAR_SCHED_INTS) sched[threadIdx.x] = 0;
 }
 
+// Rotate-half RoPE of this lane's Q fragments from a cos/sin table in LDS:
+// (cos, sin) of position r (relative to the item's first row) and frequency
+// j at tab[j][r] (two floats), frequencies 0..31 in tlo, 32..63 in thi, NR
+// positions per frequency.  Same angles and rotation as rope_q.
+__device__ __forceinline__ void rope_q_tab(bf16x8* qf, int r, int hf, int NR, int tlo,
+                                           int thi) {
+#pragma unroll
+  for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 16 * dc + 8 * hf + e;
+      const int addr = (j < 32 ? tlo + j * NR * 8 : thi + (j - 32) * NR * 8) + r * 8;
+      const f32x2 cs = *lds_ptr<f32x2>(addr);
+      float y1, y2;
+      rope_rotate((float)qf[dc][e], (float)qf[dc + 4][e], cs.x, cs.y, y1, y2);
+      qf[dc][e] = (__bf16)y1;
+      qf[dc + 4][e] = (__bf16)y2;
+    }
+}
+
 __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // tile buffer b: K rows at smK + b TILE, V rows at smV + b TILE
   __shared__ __attribute__((aligned(1024))) uint8_t smK[NBUF * TILE];
@@ -217,21 +237,8 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   const int64_t qpos = qrow + p.pos_shift;
 
   // Q^T operands (B of S^T = K Q^T): lane (query l32, half hf) holds
-  // d = 16dc + 8hf .. +7
+  // d = 16dc + 8hf .. +7 (loaded in the prologue, beside the first tile)
   bf16x8 qf[D / 16];
-  {
-    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q.data) + (int64_t)it.b * p.q.sB +
-                       (int64_t)head * p.q.sH + (row_ok ? qrow : 0) * p.q.sS;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      u32x4 v = {0, 0, 0, 0};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qr + 16 * dc + 8 * hf);
-      qf[dc] = as_bf16x8(v);
-    }
-    // complete the Q loads before any (untracked) tile DMA is in flight, so
-    // the compiler never needs a vmcnt wait for them inside the key loop
-    __builtin_amdgcn_s_waitcnt(0);
-  }
 
   // ---- per-lane constant LDS offsets
   // K read for S^T: row 32kb + l32, logical chunk 2dc + hf
@@ -431,10 +438,51 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // column has a finite max, then 2^8
   float plim = -1.f;
 
-  // prologue: tiles 0 and 1 in flight, wait for tile 0, first S
+  // prologue: tile 0 in flight while Q loads, then tile 1, RoPE, first S
   if (nt > 0) load_next(0);
+  {
+    // a lane past the last row reads row 0 instead (in bounds; its
+    // results are never stored)
+    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q.data) + (int64_t)it.b * p.q.sB +
+                       (int64_t)head * p.q.sH + (row_ok ? qrow : 0) * p.q.sS;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+      qf[dc] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * dc + 8 * hf));
+    // complete the Q loads (and tile 0, issued before them) here, so the
+    // compiler, which does not count the untracked tile DMAs, has no load of
+    // its own left to wait for later
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   if (nt > 1) load_next(1);
-  if (p.q_rope) rope_q(qf, (double)qpos, hf, p.inv_freq);   // under the tile loads
+  // RoPE of Q, under the tile loads.  With 4 or more query heads per
+  // workgroup, the workgroup's (at most 64) positions are shared by several
+  // waves: each (position, frequency) angle is then computed once, into the
+  // third tile slot (not loaded before the first barrier of the key loop),
+  // and read back by every wave of that position.
+  if (p.q_rope) {
+    if (p.gw >= 4) {
+      const int NR = 32 * p.npg;                    // 32 or 64 positions
+      const int tlo = (int)lds_u32(smK + 2 * TILE), thi = (int)lds_u32(smV + 2 * TILE);
+      // wave w: frequencies w, w + 8, ..., lane = position.  The frequency
+      // is wave-uniform, so its load is a scalar one and the compiler's
+      // wait for it does not also wait for the tile DMAs in flight.
+      if (lane < NR) {
+        const double pos = (double)(it.qr0 + lane + p.pos_shift);
+#pragma unroll 2
+        for (int k = 0; k < 8; ++k) {
+          const int j = wave + 8 * k;
+          float c, sn;
+          rope_angle(pos, p.inv_freq[j], c, sn);
+          const int addr = (j < 32 ? tlo + j * NR * 8 : thi + (j - 32) * NR * 8) + lane * 8;
+          *(__attribute__((address_space(3))) f32x2*)(uintptr_t)(uint32_t)addr = f32x2{c, sn};
+        }
+      }
+      __syncthreads();
+      rope_q_tab(qf, 32 * pg + l32, hf, NR, tlo, thi);
+    } else {
+      rope_q(qf, (double)qpos, hf, p.inv_freq);
+    }
+  }
   if (nt > 1) wait_vm_keep4(); else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 s = {};
