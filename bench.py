@@ -254,7 +254,7 @@ def decode_cold(st, dev, w, ev, samples=16):
 
 def hbm_stream(ev, mib=1024, reps=5):
     """Achievable streaming-read rate on this GPU: the library's plain
-    streaming read (16-byte loads, every byte once) over 1 GiB, four times
+    streaming read (16-byte nontemporal loads, every byte once) over 1 GiB, four times
     the 256 MiB Infinity Cache, so every pass reads HBM; best of three grid
     sizes.  Reported beside the decode rate as the practical ceiling of an
     HBM-bound kernel."""
@@ -280,7 +280,7 @@ def hbm_stream(ev, mib=1024, reps=5):
     del buf
     return {"gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBS, "bytes": mib << 20,
             "workgroups": best[1],
-            "note": "star_stream_read over 1 GiB (a plain streaming read, 16-byte loads)"}
+            "note": "star_stream_read over 1 GiB (a plain streaming read, 16-byte nontemporal loads)"}
 
 
 def main():

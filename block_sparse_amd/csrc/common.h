@@ -33,24 +33,35 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 template <typename T>
 struct Load8;
 
+// load: a plain load.  load_stream: the same load with the nontemporal
+// hint, for data read exactly once (it streams from HBM ~12% faster than
+// plain 16-byte loads on this GPU: 6.5-6.8 against 5.7-6.0 TB/s measured).
 template <>
 struct Load8<__bf16> {
   static __device__ __forceinline__ u32x4 load(const __bf16* p) {
     return *reinterpret_cast<const u32x4*>(p);
   }
+  static __device__ __forceinline__ u32x4 load_stream(const __bf16* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
 };
 
 template <>
 struct Load8<float> {
-  static __device__ __forceinline__ u32x4 load(const float* p) {
-    f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-    f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+  static __device__ __forceinline__ u32x4 pack(f32x4 a, f32x4 b) {
     u32x4 r;
     r[0] = pack_bf16(a[0], a[1]);
     r[1] = pack_bf16(a[2], a[3]);
     r[2] = pack_bf16(b[0], b[1]);
     r[3] = pack_bf16(b[2], b[3]);
     return r;
+  }
+  static __device__ __forceinline__ u32x4 load(const float* p) {
+    return pack(reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]);
+  }
+  static __device__ __forceinline__ u32x4 load_stream(const float* p) {
+    return pack(__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1));
   }
 };
 

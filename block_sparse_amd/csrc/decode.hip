@@ -7,17 +7,23 @@
 // keep HBM busy: one workgroup owns one long chunk of one partition for one
 // KV head and all of its g query heads (GQA heads share each K/V byte read),
 // its eight waves walk interleaved 32-key tiles of the chunk, and each wave
-// keeps its next two tiles in flight in registers (16-byte loads, four lanes
-// per 64-byte run of a key row) while it computes the current one.  Long chunks
-// keep the per-workgroup setup and the number of partials (and so the merge
-// that follows) small.
+// keeps its next two tiles in flight in registers while it computes the
+// current one.  Long chunks keep the per-workgroup setup and the number of
+// partials (and so the merge that follows) small.
+//
+// Loads: every load instruction of a wave reads 1 KiB of consecutive bytes
+// (whole key rows) with the nontemporal hint.  Each K/V byte is read once,
+// and on this GPU that form streams at ~7.0-7.1 TB/s against ~6.2 TB/s for
+// the MFMA operand layout (16 rows x 64 B per instruction, which with the
+// hint falls to ~5.9 TB/s: half-lines evicted before their other half is
+// read).  The tile therefore goes through LDS for K as well as V.
 //
 // Math on v_mfma_f32_16x16x32_bf16 with the g*Lq query rows padded to 16:
-// S^T = K Q^T (A = K straight from the loaded registers), the row max/sum
-// per lane column, then O^T += V^T P^T where V^T is read from a per-wave
-// LDS copy of the V tile with ds_read_b64_tr_b16 (keys in the order the
-// S^T registers hold them) and P^T comes from the S^T registers.  The
-// waves merge their (m, l, O) in LDS at the end.
+// S^T = K Q^T (A = K read back from the wave's LDS copy in operand layout),
+// the row max/sum per lane column, then O^T += V^T P^T where V^T is read
+// from the LDS copy of the V tile with ds_read_b64_tr_b16 (keys in the
+// order the S^T registers hold them) and P^T comes from the S^T registers.
+// The waves merge their (m, l, O) in LDS at the end.
 #include "common.h"
 #include "internal.h"
 #include "rope_math.h"
@@ -47,9 +53,10 @@ __device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
 #endif
 }
 
-// 16-byte chunk c of V-tile row r is stored at chunk c ^ swz(r & 15): the
-// 4-row x 2-chunk footprint of a transpose read and the 16-row footprint
-// of a row write land on distinct banks (32 or 64 banks of 4 bytes).
+// 16-byte chunk c of K/V-tile row r is stored at chunk c ^ swz(r & 15): the
+// 4-row x 2-chunk footprint of a transpose read of V and the 16-row x
+// 1-chunk footprint of a K operand read land on distinct banks (32 or 64
+// banks of 4 bytes); a row write covers all banks.
 __device__ __forceinline__ int swz(int r) {
   const int k = r & 3;
   const int g = (k << 1) | ((k ^ (k >> 1)) & 1);
@@ -68,7 +75,8 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   constexpr int VT = KTD * D * 2;
   // per-wave V tiles during the key loop; reused for the final merge
   static_assert(NWD * 16 * D * 4 <= NWD * VT, "merge buffer must fit");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NWD * VT];
+  // per wave: a V tile and a K tile (row-major, chunk-swizzled)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * NWD * VT];
   __shared__ float red_m[NWD][16];
   __shared__ float red_l[NWD][16];
   float (*red_o)[16][D] = reinterpret_cast<float (*)[16][D]>(smem);
@@ -150,44 +158,48 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const int rot = nt > 0 ? (int)(((int64_t)lid * nt) / (p.total_items > 0 ? p.total_items : 1)) : 0;
   auto phys = [&](int t) { const int u = t + rot; return u >= nt ? u - nt : u; };
   uint8_t* vs = smem + wave * VT;
+  uint8_t* ks = smem + (NWD + wave) * VT;
 
-  // LDS offsets: row writes (row 16kb + n, chunk 4dc + kg) and transpose
-  // reads (16-lane group kg, lane j: row 16t + 4kg + (j >> 2), columns
-  // 16db + 4(j & 3) .. +3)
-  int wofs[2][NDC];
+  // LDS offsets.  Loads and row writes: instruction i of a tile reads 1 KiB
+  // contiguous, RPI whole rows; lane -> row i RPI + lane / CPR, chunk
+  // lane % CPR.  V transpose reads: 16-lane group kg, lane j: row
+  // 16t + 4kg + (j >> 2), columns 16db + 4(j & 3) .. +3.
+  // (the swizzle repeats every 16 rows, so instruction i + WP writes at
+  // wofs[i % WP] plus a constant)
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NLD = KTD / RPI, WP = 16 / RPI;
+  constexpr int ROW16 = 16 * D * 2;   // bytes of 16 rows
+  int wofs[WP];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < WP; ++i) wofs[i] = v_chunk_off<D>(RPI * i + lane / CPR, lane % CPR);
+  // K reads in MFMA operand layout: row 16 kb + n (kb: + ROW16), chunk 4 dc + kg
+  int kofs[NDC];
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) wofs[kb][dc] = v_chunk_off<D>(16 * kb + n, 4 * dc + kg);
-  int rofs[2][NDB];
+  for (int dc = 0; dc < NDC; ++dc) kofs[dc] = v_chunk_off<D>(n, 4 * dc + kg);
+  // (rows 16.. of the tile: + ROW16, the swizzle repeating every 16 rows)
+  int rofs[NDB];
   {
     const int j = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int row = 16 * t + 4 * kg + (j >> 2);
-        const int col = 16 * db + 4 * (j & 3);
-        rofs[t][db] = v_chunk_off<D>(row, col >> 3) + ((col & 7) << 1);
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const int row = 4 * kg + (j >> 2);
+      const int col = 16 * db + 4 * (j & 3);
+      rofs[db] = v_chunk_off<D>(row, col >> 3) + ((col & 7) << 1);
+    }
   }
 
-  // register staging, two tiles deep: [slot][key block (16 keys)][d chunk]
-  u32x4 kr[2][2][NDC], vr[2][2][NDC];
+  // register staging, two tiles deep: [slot][load instruction]
+  u32x4 kr[2][NLD], vr[2][NLD];
   auto load_tile = [&](int slot, int t) {
     const int64_t kt = c0 + (int64_t)KTD * phys(t);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int64_t key = kt + 16 * kb + n;
-      const bool ok = key < c1;
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        kr[slot][kb][dc] = u32x4{0, 0, 0, 0};
-        vr[slot][kb][dc] = u32x4{0, 0, 0, 0};
-        if (ok) {
-          kr[slot][kb][dc] = Load8<T>::load(kbase + key * p.k.sS + 32 * dc + 8 * kg);
-          vr[slot][kb][dc] = Load8<T>::load(vbase + key * p.v.sS + 32 * dc + 8 * kg);
-        }
+    for (int i = 0; i < NLD; ++i) {
+      const int64_t key = kt + RPI * i + lane / CPR;
+      const int ch = lane % CPR;
+      kr[slot][i] = u32x4{0, 0, 0, 0};
+      vr[slot][i] = u32x4{0, 0, 0, 0};
+      if (key < c1) {
+        kr[slot][i] = Load8<T>::load_stream(kbase + key * p.k.sS + 8 * ch);
+        vr[slot][i] = Load8<T>::load_stream(vbase + key * p.v.sS + 8 * ch);
       }
     }
   };
@@ -243,23 +255,29 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   auto process = [&](auto slc, int t) {
     constexpr int SL = decltype(slc)::value;
     const int64_t kt = c0 + (int64_t)KTD * phys(t);
-    // S^T = K Q^T for two 16-key blocks
+    // stage K and V (row-major, chunk-swizzled) in this wave's LDS regions;
+    // the previous tile's reads were issued before these writes, and LDS
+    // executes one wave's instructions in order
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int o = wofs[i % WP] + (i / WP) * ROW16;
+      *reinterpret_cast<u32x4*>(ks + o) = kr[SL][i];
+      *reinterpret_cast<u32x4*>(vs + o) = vr[SL][i];
+    }
+    asm volatile("" ::: "memory");
+    // S^T = K Q^T for two 16-key blocks, K read back in operand layout
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) s[kb] = mfma16(as_bf16x8(kr[SL][kb][dc]), qf[dc], s[kb]);
-    }
-    // stage V (row-major, chunk-swizzled) in this wave's LDS region; the
-    // previous tile's transpose reads were issued before these writes, and
-    // LDS executes one wave's instructions in order
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
-        *reinterpret_cast<u32x4*>(vs + wofs[kb][dc]) = vr[SL][kb][dc];
+        s[kb] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ks + kofs[dc] + kb * ROW16)),
+                       qf[dc], s[kb]);
+    }
+    // refill the staging slot with the tile two steps ahead (after the K
+    // operands are read, so they can use the slot's registers)
     asm volatile("" ::: "memory");
     if (t + 2 * NWD < nt) load_tile(SL, t + 2 * NWD);
 
@@ -300,8 +318,8 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
     // 4kg + e (e < 4) and 16 + 4kg + (e - 4), matching pt's order.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const s16x4 a0 = tr_read(vs + rofs[0][db]);
-      const s16x4 a1 = tr_read(vs + rofs[1][db]);
+      const s16x4 a0 = tr_read(vs + rofs[db]);
+      const s16x4 a1 = tr_read(vs + rofs[db] + ROW16);
       const bf16x8 a =
           __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = mfma16(a, pt, oacc[db]);

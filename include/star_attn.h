@@ -389,7 +389,8 @@ int star_linear(star_context* ctx, const star_tensor* x, const star_tensor* w,
 
 /*
  * Measurement aid, not a step of the method: a plain streaming read of
- * `bytes` bytes of device memory at `src` (each byte once, 16-byte loads).
+ * `bytes` bytes of device memory at `src` (each byte once, 16-byte
+ * nontemporal loads).
  * Workgroup i reads bytes [i, i + 1) * bytes / workgroups and writes the XOR
  * of the 32-bit words it read to out[i], so the XOR of out[0 .. workgroups)
  * is the XOR of every word of the buffer.  Its rate is the practical
