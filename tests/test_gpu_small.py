@@ -111,20 +111,29 @@ def test_phase1_sched_identical(case):
     q, k, v = (to_dev(t) for t in _qkv(23, B, Hq, Hkv, L, D, bf16, 1.0))
     sched = torch.full((sa.SCHED_INTS,), 12345, dtype=torch.int32, device=q.device)
     sched[::3] = -7
+
+    def nan_out():
+        # outputs start as NaN, so an item the queues never hand out shows
+        o = torch.full((B, Hq, L, D), float("nan"), dtype=torch.bfloat16, device=q.device)
+        return o, torch.full((B, Hq, L), float("nan"), dtype=torch.float32, device=q.device)
+
     o0, l0 = sa.phase1_blocklocal(q, k, v, b, a, want_lse=True)
     for rep in range(3):
-        o1, l1 = sa.phase1_blocklocal(q, k, v, b, a, want_lse=True, sched=sched)
+        o1, l1 = nan_out()
+        sa.phase1_blocklocal(q, k, v, b, a, out=o1, lse=l1, sched=sched)
         torch.cuda.synchronize()
         assert torch.equal(o0, o1) and torch.equal(l0, l1), f"blocklocal, call {rep}"
     n = -(-L // b)
     st, ln = [0] * n, [0] + [min(a, L)] * (n - 1)
     p0, pl0 = sa.phase1_prefix(q, k, v, k, v, st, ln, b, want_lse=True)
-    p1, pl1 = sa.phase1_prefix(q, k, v, k, v, st, ln, b, want_lse=True, sched=sched)
+    p1, pl1 = nan_out()
+    sa.phase1_prefix(q, k, v, k, v, st, ln, b, out=p1, lse=pl1, sched=sched)
     torch.cuda.synchronize()
     assert torch.equal(p0, p1) and torch.equal(pl0, pl1), "prefix"
     if D == 128 and bf16:
         r0, rl0 = sa.phase1_rope(q, k, v, b, a, want_lse=True)
-        r1, rl1 = sa.phase1_rope(q, k, v, b, a, want_lse=True, sched=sched)
+        r1, rl1 = nan_out()
+        sa.phase1_rope(q, k, v, b, a, out=r1, lse=rl1, sched=sched)
         torch.cuda.synchronize()
         assert torch.equal(r0, r1) and torch.equal(rl0, rl1), "rope"
 
