@@ -34,6 +34,12 @@
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
+//  * with q_rope the kernel rotates Q itself in its prologue, under the
+//    first tile loads (per lane, or from a per-workgroup cos/sin table when
+//    4 or more query heads share the workgroup's positions).
+//  * work items come in a fixed XCD-aware order, or, with a scheduling
+//    workspace, from per-XCD queues (sched_grab), so that XCDs running at
+//    a higher clock take over the slower ones' remaining items.
 // One workgroup = 8 waves, one 32-row column block each; 64-key tiles in
 // three LDS buffers (one tile computing, one landing, one free); two waves
 // share a SIMD, so one's LDS reads, barrier waits and exps run under the
