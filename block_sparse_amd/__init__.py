@@ -246,14 +246,17 @@ def pulsar_prefix(tokens, L: int, block_b: int, chunk_m: int = 32, sink: int = 6
     tptr = tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     lib = library()
     args = (tptr, int(L), int(block_b), int(chunk_m), int(sink), int(k))
-    r = lib.star_pulsar_prefix(*args, None, 0, ctypes.byref(nrows), st.ctypes.data_as(P64),
-                               ln.ctypes.data_as(P64), int(n))
-    if r not in (0, _lib.STATUS_CODE["STAR_ERR_SHAPE"]):
-        _lib.check("star_pulsar_prefix", r)
-    rows = np.zeros(max(nrows.value, 1), dtype=np.int64)
+    # at most the sink plus k chunks of every block but the last
+    cap = min(L, min(sink, block_b, L) + max(n - 1, 0) * max(k, 0) * chunk_m)
+    rows = np.zeros(max(cap, 1), dtype=np.int64)
     r = lib.star_pulsar_prefix(*args, rows.ctypes.data_as(P64), int(rows.size),
                                ctypes.byref(nrows), st.ctypes.data_as(P64),
                                ln.ctypes.data_as(P64), int(n))
+    if r == _lib.STATUS_CODE["STAR_ERR_SHAPE"] and nrows.value > rows.size:
+        rows = np.zeros(nrows.value, dtype=np.int64)
+        r = lib.star_pulsar_prefix(*args, rows.ctypes.data_as(P64), int(rows.size),
+                                   ctypes.byref(nrows), st.ctypes.data_as(P64),
+                                   ln.ctypes.data_as(P64), int(n))
     _lib.check("star_pulsar_prefix", r)
     return rows[:nrows.value], st[:n], ln[:n]
 

@@ -5,6 +5,7 @@
 // argument", "Core claim", "Assumptions & free parameters").  Integer work
 // over the token ids only; the pages run it on the CPU.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <unordered_map>
@@ -36,17 +37,45 @@ extern "C" int star_pulsar_prefix(const int32_t* tokens, int64_t L, int64_t bloc
   }
   if (tokens == nullptr || prefix_start == nullptr || prefix_len == nullptr) return STAR_ERR_NULL;
   try {
-    // df(t): number of blocks that contain t
-    std::unordered_map<int32_t, int64_t> df;
-    df.reserve((size_t)std::min<int64_t>(L, 1 << 22));
-    std::vector<int32_t> blk;
-    for (int64_t i = 0; i < n; ++i) {
-      const int64_t s = i * block_b, e = std::min(s + block_b, L);
-      blk.assign(tokens + s, tokens + e);
-      std::sort(blk.begin(), blk.end());
-      blk.erase(std::unique(blk.begin(), blk.end()), blk.end());
-      for (int32_t t : blk) ++df[t];
+    // df(t): number of blocks that contain t.  Token ids of a real
+    // vocabulary are small non-negative integers: then one pass with a
+    // dense count and the last block that counted each id; otherwise a
+    // hash map over each block's distinct ids.
+    int32_t tmin = INT32_MAX, tmax = INT32_MIN;
+    for (int64_t t = 0; t < L; ++t) {
+      tmin = std::min(tmin, tokens[t]);
+      tmax = std::max(tmax, tokens[t]);
     }
+    const bool dense = tmin >= 0 && tmax < (1 << 24);
+    std::vector<int64_t> df_dense;
+    std::unordered_map<int32_t, int64_t> df_map;
+    if (dense) {
+      df_dense.assign((size_t)tmax + 1, 0);
+      std::vector<int64_t> last((size_t)tmax + 1, -1);
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = i * block_b, e = std::min(s + block_b, L);
+        for (int64_t t = s; t < e; ++t) {
+          const int32_t id = tokens[t];
+          if (last[(size_t)id] != i) {
+            last[(size_t)id] = i;
+            ++df_dense[(size_t)id];
+          }
+        }
+      }
+    } else {
+      df_map.reserve((size_t)std::min<int64_t>(L, 1 << 22));
+      std::vector<int32_t> blk;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = i * block_b, e = std::min(s + block_b, L);
+        blk.assign(tokens + s, tokens + e);
+        std::sort(blk.begin(), blk.end());
+        blk.erase(std::unique(blk.begin(), blk.end()), blk.end());
+        for (int32_t t : blk) ++df_map[t];
+      }
+    }
+    auto df = [&](int32_t id) -> int64_t {
+      return dense ? df_dense[(size_t)id] : df_map[id];
+    };
     const int64_t sink_n = std::min<int64_t>(std::min<int64_t>(sink, block_b), L);
     // summary of every block but the last (no later block reads it)
     std::vector<std::vector<int64_t>> summary(n);
@@ -58,7 +87,7 @@ extern "C" int star_pulsar_prefix(const int32_t* tokens, int64_t L, int64_t bloc
         if (i == 0 && c0 < sink_n) continue;     // already in the sink
         const int64_t c1 = std::min<int64_t>(c0 + chunk_m, e);
         int64_t dmin = INT64_MAX;
-        for (int64_t t = c0; t < c1; ++t) dmin = std::min(dmin, df[tokens[t]]);
+        for (int64_t t = c0; t < c1; ++t) dmin = std::min(dmin, df(tokens[t]));
         // max over the chunk of log(n / max(df, 1)) is reached at the
         // smallest df
         cand.push_back({std::log((double)n / (double)std::max<int64_t>(dmin, 1)), c0, c1});

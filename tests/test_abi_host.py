@@ -252,6 +252,13 @@ def test_pulsar_prefix_host_matches_oracle(lib):
         r1, s1, l1 = sa.pulsar_prefix(tok, L, b, m, sink, k)
         r2, s2, l2 = so.pulsar_prefix(tok, L, b, m, sink, k)
         assert np.array_equal(r1, r2) and np.array_equal(s1, s2) and np.array_equal(l1, l2)
+        # ids outside a dense vocabulary range (negative, >= 2^24) take the
+        # library's hash-map path: same selection
+        wide = np.where(tok % 3 == 0, -tok - 1, tok * 1000 + 7).astype(np.int64)
+        wide = np.where(wide > 2 ** 31 - 1, wide % (2 ** 31 - 1), wide).astype(np.int32)
+        assert len(np.unique(wide)) == len(np.unique(tok))     # still a relabelling
+        r3, s3, l3 = sa.pulsar_prefix(wide, L, b, m, sink, k)
+        assert np.array_equal(r3, r2) and np.array_equal(s3, s2) and np.array_equal(l3, l2)
 
 
 def test_pulsar_prefix_host_validation(lib):
