@@ -34,6 +34,7 @@ P1_CASES = [
     (1, 24, 8, 128, 300, 100, 100, True, 1.0),     # g = 3
     (1, 5, 5, 64, 97, 32, 32, True, 1.0),          # L < one key tile
     (1, 8, 2, 128, 1, 16, 16, True, 1.0),          # one token
+    (1, 8, 2, 128, 600, 200, 200, False, 0.125),   # D = 128, fp32 inputs (flash.hip)
 ]
 
 
@@ -200,6 +201,7 @@ P2_CASES = [
     (1, 8, 1, 128, 300, 3, 64, 16),     # flash path (g*Lq = 24), many empty chunks
     (2, 8, 2, 128, 777, 1, 200, 4, False),   # decode path, fp32 inputs (rounded at load)
     (1, 4, 1, 64, 300, 1, 100, 8, False),    # decode path, D = 64, fp32 inputs
+    (1, 16, 2, 128, 500, 16, 128, 2, False),  # flash path (g*Lq = 128), D = 128, fp32 inputs
 ]
 
 
