@@ -57,6 +57,8 @@ P1_ROPE_CASES = [
     (1, 32, 8, 1000, 256, 256),    # Llama-8B heads
     (1, 8, 1, 333, 1000, 1000),    # one block
     (1, 16, 16, 130, 64, 0),       # MHA, no anchor
+    (1, 8, 4, 450, 128, 128),      # g = 2: per-lane angles, 128 positions per workgroup
+    (1, 32, 2, 300, 100, 100),     # g = 16: cos/sin table, two head groups per KV head
 ]
 
 
