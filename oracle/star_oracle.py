@@ -49,6 +49,7 @@ Readings where the pages leave a step open (all listed in the design notes):
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -60,9 +61,28 @@ NEG_INF = -np.inf
 # RoPE at original position ids
 # ----------------------------------------------------------------------------
 def rope_theta(D: int, base: float) -> np.ndarray:
-    """Rotation frequencies theta_j = base^(-2j/D), j = 0..D/2-1 (float64)."""
-    j = np.arange(D // 2, dtype=np.float64)
-    return np.power(np.float64(base), -2.0 * j / D)
+    """Rotation frequencies theta_j = base^(-2j/D), j = 0..D/2-1: each one
+    the float64 value nearest the exact power.
+
+    The power is evaluated as exp(-(2j/D) ln(base)) in 40-digit decimal
+    arithmetic and rounded once to float64 (Python's Decimal -> float
+    conversion rounds to nearest).  numpy's vectorised ``power`` is not
+    used: on hosts with AVX-512 it dispatches to a SIMD routine that is off
+    by one ulp for some j (2 of the 64 frequencies at base 500000, D = 128),
+    so its angles, and the bf16 rounding of rotated values, would depend on
+    the host the oracle runs on.
+    """
+    return np.array(_rope_theta_exact(int(D), float(base)), dtype=np.float64)
+
+
+@functools.lru_cache(maxsize=64)
+def _rope_theta_exact(D: int, base: float) -> tuple:
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 40
+        ln_base = Decimal(base).ln()                 # Decimal(float) is exact
+        return tuple(float((ln_base * Decimal(-2 * j) / Decimal(D)).exp())
+                     for j in range(D // 2))
 
 
 def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:

@@ -59,6 +59,25 @@ def test_rope_pairs_and_frequencies():
     assert np.allclose(out[0], [math.cos(10.0), 0.0, math.sin(10.0), 0.0], atol=1e-12)
 
 
+def test_rope_theta_is_the_nearest_float64():
+    """theta_j = base^(-2j/D), each the float64 nearest the exact power.
+    Bases that are powers of two give exactly representable frequencies
+    (2^16 at D = 8: theta_j = 2^(-4j)); theta_0 = 1 for any base; and for
+    the bases and head dims the workloads use, the C library's pow (a
+    separate routine, correctly rounded on these inputs) gives the same
+    bits -- numpy's vectorised power does not on AVX-512 hosts, which is why
+    the oracle avoids it."""
+    assert so.rope_theta(8, 65536.0).tolist() == [1.0, 2.0 ** -4, 2.0 ** -8, 2.0 ** -12]
+    assert so.rope_theta(2, 12345.0).tolist() == [1.0]
+    for base in (100.0, 10000.0, 500000.0, 1e6):
+        for D in (2, 4, 16, 64, 128):
+            th = so.rope_theta(D, base)
+            ref = [math.pow(base, -2.0 * j / D) for j in range(D // 2)]
+            assert th.tolist() == ref, (base, D)
+    # a slip in the exponent (-j/D instead of -2j/D) is caught
+    assert so.rope_theta(8, 65536.0)[1] != 2.0 ** -2
+
+
 def test_rope_identity_norm_relative_complex():
     D, S = 128, 33
     x = rand(S, D)
