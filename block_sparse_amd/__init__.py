@@ -21,7 +21,7 @@ import torch
 from . import _lib
 from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 
-__all__ = ["rope_apply", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
+__all__ = ["rope_apply", "rope_freqs", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
            "phase1_prefix", "sched_workspace", "SCHED_INTS",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
            "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
@@ -95,6 +95,14 @@ def rope_apply(x: torch.Tensor, pos: torch.Tensor | None = None, pos0: int = 0,
                                    float(base), _stream(x))
     _lib.check("star_rope_apply", st)
     return out
+
+
+def rope_freqs(D: int, base: float = 500000.0):
+    """The RoPE frequencies theta_j (fp64, j < D/2) every rotating entry
+    point uses, as a list of floats (host call, no GPU needed)."""
+    out = (ctypes.c_double * max(D // 2, 1))()
+    _lib.check("star_rope_freqs", library().star_rope_freqs(int(D), float(base), out))
+    return list(out)[:D // 2]
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, slot0: int, pos0: int,
@@ -320,8 +328,8 @@ def lse_merge(o_part, lse_part, out=None, lse=None, out_dtype=torch.float32,
                             or lse.numel() != B * H * S):
         raise ValueError("lse must be a contiguous fp32 tensor of B*H*S rows")
     do = _desc(out)
-    st = library().star_lse_merge(_ptr(o_part), _ptr(lse_part), int(N), ctypes.byref(do),
-                                  _ptr(lse), _stream(o_part))
+    st = library().star_lse_merge(_ptr(o_part), _ptr(lse_part), int(N), int(B), int(H), int(S),
+                                  int(D), ctypes.byref(do), _ptr(lse), _stream(o_part))
     _lib.check("star_lse_merge", st)
     return out, lse
 

@@ -24,7 +24,7 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # every symbol include/star_attn.h declares
-EXPORTS = ("star_rope_apply", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
+EXPORTS = ("star_rope_apply", "star_rope_freqs", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase1_prefix", "star_phase1_rope", "star_gather_rows", "star_stream_read", "star_pulsar_prefix",
            "star_phase2_partial", "star_lse_merge", "star_decode_step",
            "star_context_create", "star_context_destroy", "star_rmsnorm", "star_linear",
@@ -50,6 +50,7 @@ _i32, _i64, _f32, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.
 
 _SIGS = {
     "star_rope_apply": (ctypes.c_int, [_T, _T, _vp, _i64, _f64, _vp]),
+    "star_rope_freqs": (ctypes.c_int, [_i64, _f64, _P(_f64)]),
     "star_kv_append": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_decode_prepare": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _vp]),
     "star_phase1_blocklocal": (ctypes.c_int, [_T, _T, _T, _i64, _i64, _f32, _T, _vp, _vp, _vp]),
@@ -63,7 +64,7 @@ _SIGS = {
                                           _P(_i64), _P(_i64), _P(_i64), _i32]),
     "star_phase2_partial": (ctypes.c_int, [_T, _T, _T, _P(_i64), _i32, _i32, _i64, _f32,
                                            _vp, _vp, _vp]),
-    "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _T, _vp, _vp]),
+    "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _i64, _T, _vp, _vp]),
     "star_decode_step": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _P(_i64), _i32,
                                         _i32, _f32, _vp, _vp, _T, _vp, _vp]),
     "star_context_create": (ctypes.c_int, [_P(_vp)]),

@@ -36,8 +36,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? STAR_OK : STAR_ERR_HIP; 
 
 bool rope_dim_ok(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 
+// theta_j = base^(-2j/D), j < D/2: the power in extended precision (x87
+// long double, 64-bit significand, error ~2^-63 relative), rounded once to
+// fp64, so theta_j is the fp64 value nearest the exact power unless that
+// power lies within ~2^-10 ulp of a rounding midpoint.  Every rotating
+// kernel forms its angle as the IEEE product pos * theta_j from these.
 void fill_inv_freq(double* inv_freq, int64_t D, double base) {
-  for (int64_t j = 0; j < D / 2; ++j) inv_freq[j] = std::pow(base, -2.0 * (double)j / (double)D);
+  for (int64_t j = 0; j < D / 2; ++j)
+    inv_freq[j] = (double)std::pow((long double)base,
+                                   -2.0L * (long double)j / (long double)D);
   for (int64_t j = D / 2; j < 64; ++j) inv_freq[j] = 0.0;
 }
 
@@ -169,7 +176,17 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 300; }
+int star_abi_version(void) { return 400; }
+
+int star_rope_freqs(int64_t D, double base, double* inv_freq) {
+  if (inv_freq == nullptr) return STAR_ERR_NULL;
+  if (!rope_dim_ok(D)) return STAR_ERR_UNSUPPORTED;
+  if (!(base > 1.0) || !std::isfinite(base)) return STAR_ERR_SHAPE;
+  double f[64];
+  fill_inv_freq(f, D, base);
+  for (int64_t j = 0; j < D / 2; ++j) inv_freq[j] = f[j];
+  return STAR_OK;
+}
 
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out, const int64_t* pos,
                     int64_t pos0, double base, void* stream) {
@@ -462,7 +479,8 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
   if (o->B != q_new->B || o->H != q_new->H || o->S != 1 || o->D != q_new->D) return STAR_ERR_SHAPE;
   int64_t chunk[STAR_MAX_PARTS];
   if ((s = check_parts(part_offsets, P, splits, k_cache->S, chunk)) != STAR_OK) return s;
-  if (slot < part_offsets[0] || slot >= part_offsets[P] || pos < 0) return STAR_ERR_SHAPE;
+  // position-contiguous cache: the token's row is its position
+  if (slot != pos || slot < part_offsets[0] || slot >= part_offsets[P]) return STAR_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
   if (rope && !(std::isfinite(base) && base > 1.0)) return STAR_ERR_SHAPE;
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
@@ -476,16 +494,7 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
   p.kn = ref(k_new);
   p.vn = ref(v_new);
   p.slot = slot;
-  if (p.rope) {
-    // the token's angles, exact in fp64, rounded once to fp32
-    double inv_freq[64];
-    fill_inv_freq(inv_freq, q_new->D, base);
-    for (int64_t j = 0; j < q_new->D / 2; ++j) {
-      const double a = (double)pos * inv_freq[j];
-      p.rc[j] = (float)std::cos(a);
-      p.rs[j] = (float)std::sin(a);
-    }
-  }
+  if (p.rope) fill_inv_freq(p.inv_freq, q_new->D, base);
   if ((s = hip_status(star::launch_decode(p, (hipStream_t)stream))) != STAR_OK) return s;
   // the merge runs as the next launch on the same stream: the kernel
   // boundary makes every workgroup's partial visible to it
@@ -533,12 +542,14 @@ int star_rmsnorm(const star_tensor* x, const void* gamma, float eps, const star_
   return hip_status(star::launch_rmsnorm(p, (hipStream_t)stream));
 }
 
-int star_lse_merge(const float* o_part, const float* lse_part, int32_t N, const star_tensor* o,
-                   float* lse, void* stream) {
+int star_lse_merge(const float* o_part, const float* lse_part, int32_t N, int64_t B,
+                   int64_t Hq, int64_t Lq, int64_t D, const star_tensor* o, float* lse,
+                   void* stream) {
   if (o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
   int s;
   if ((s = check_tensor(o, true)) != STAR_OK) return s;
   if (N < 1 || N > 65536) return STAR_ERR_SHAPE;
+  if (o->B != B || o->H != Hq || o->S != Lq || o->D != D) return STAR_ERR_SHAPE;
   if (o->D != 64 && o->D != 128) return STAR_ERR_UNSUPPORTED;
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return STAR_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;

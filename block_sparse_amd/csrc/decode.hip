@@ -97,6 +97,9 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const int64_t c0 = p.offs[part] + (int64_t)sp * p.chunk[part];
   int64_t c1 = min(c0 + p.chunk[part], p.offs[part + 1]);
   c1 = min(c1, p.kv_rows);
+  // rows after the last query position are visible to no row: never read
+  // them (they may be cache slots not written yet)
+  c1 = min(c1, p.q_pos0 + p.Lq);
   if (c1 < c0) c1 = c0;
 
   const int nrows = p.g * (int)p.Lq;
@@ -109,37 +112,33 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
 
   if constexpr (FUSED) {
     // the workgroup whose chunk holds the new token's slot appends its K/V
-    // row (K rotated like q) before any of its waves loads the chunk
+    // row (K rotated like q, one pair per thread) before any of its waves
+    // loads the chunk
     if (p.slot >= c0 && p.slot < c1) {
-      if (tid < D / 16) {
-        const int ch = tid, half = D / 2;
-        const __bf16* kn = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
-                           (int64_t)kvh * p.kn.sH;
-        const __bf16* vn = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
-                           (int64_t)kvh * p.vn.sH;
-        __bf16* kc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.k.data)) +
-                     (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH + p.slot * p.k.sS;
-        __bf16* vc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.v.data)) +
-                     (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH + p.slot * p.v.sS;
-        const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const u32x4*>(kn + 8 * ch));
-        const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const u32x4*>(kn + half + 8 * ch));
-        bf16x8 y1 = x1, y2 = x2;
+      const int half = D / 2;
+      const __bf16* kn = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
+                         (int64_t)kvh * p.kn.sH;
+      const __bf16* vn = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
+                         (int64_t)kvh * p.vn.sH;
+      __bf16* kc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.k.data)) +
+                   (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH + p.slot * p.k.sS;
+      __bf16* vc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.v.data)) +
+                   (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH + p.slot * p.v.sS;
+      if (tid < half) {
+        const int j = tid;
+        __bf16 y1 = kn[j], y2 = kn[j + half];
         if (p.rope) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float c = p.rc[8 * ch + e], sn = p.rs[8 * ch + e];
-            const float a1 = (float)x1[e], a2 = (float)x2[e];
-            float r1, r2;
-            rope_rotate(a1, a2, c, sn, r1, r2);
-            y1[e] = (__bf16)r1;
-            y2[e] = (__bf16)r2;
-          }
+          double c, sn, r1, r2;
+          rope_cs((double)p.q_pos0, p.inv_freq[j], c, sn);
+          rope_rotate64((double)(float)kn[j], (double)(float)kn[j + half], c, sn, r1, r2);
+          y1 = f64_to_bf16(r1);
+          y2 = f64_to_bf16(r2);
         }
-        *reinterpret_cast<bf16x8*>(kc + 8 * ch) = y1;
-        *reinterpret_cast<bf16x8*>(kc + half + 8 * ch) = y2;
+        kc[j] = y1;
+        kc[j + half] = y2;
+      } else if (tid < half + D / 8) {
+        const int ch = tid - half;
         *reinterpret_cast<u32x4*>(vc + 8 * ch) = *reinterpret_cast<const u32x4*>(vn + 8 * ch);
-        *reinterpret_cast<u32x4*>(vc + half + 8 * ch) =
-            *reinterpret_cast<const u32x4*>(vn + half + 8 * ch);
       }
       __syncthreads();   // stores complete and visible to this workgroup's loads
     }
@@ -204,14 +203,61 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
     }
   };
 
+  // fused rope: the workgroup rotates its g query rows once, one pair per
+  // thread, into an LDS copy that every wave then reads its Q^T operand
+  // from.  The raw pairs are loaded before the tile loads, so waiting for
+  // them does not wait for the tiles; the barrier waits only for the LDS
+  // writes.
+  __shared__ __attribute__((aligned(16))) __bf16 q_rot[16 * D];
+  constexpr int NPAIR = (16 * (D / 2) + NWD * 64 - 1) / (NWD * 64);   // pairs per thread
+  [[maybe_unused]] __bf16 qx1[NPAIR], qx2[NPAIR];
+  [[maybe_unused]] double qth[NPAIR];
+  const bool rope_q = FUSED && p.rope;
+  if (rope_q) {
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      const int idx = tid + NWD * 64 * i, r = idx / (D / 2), j = idx % (D / 2);
+      qx1[i] = qx2[i] = (__bf16)0.f;
+      qth[i] = p.inv_freq[j];
+      if (r < nrows) {
+        const __bf16* qr = reinterpret_cast<const __bf16*>(p.q.data) + (int64_t)b * p.q.sB +
+                           (int64_t)(kvh * p.g + r % p.g) * p.q.sH + (int64_t)(r / p.g) * p.q.sS;
+        qx1[i] = qr[j];
+        qx2[i] = qr[j + D / 2];
+      }
+    }
+  }
+
   // the first two tiles go out before the query is loaded and rotated
   // this wave's tiles: wave, wave + NWD, ...; two in flight at any time
   if (wave < nt) load_tile(0, wave);
   if (wave + NWD < nt) load_tile(1, wave + NWD);
 
+  if (rope_q) {
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      const int idx = tid + NWD * 64 * i, r = idx / (D / 2), j = idx % (D / 2);
+      if (r < 16) {
+        double c, sn, y1, y2;
+        rope_cs((double)(p.q_pos0 + r / p.g), qth[i], c, sn);
+        rope_rotate64((double)(float)qx1[i], (double)(float)qx2[i], c, sn, y1, y2);
+        q_rot[r * D + j] = f64_to_bf16(y1);
+        q_rot[r * D + j + D / 2] = f64_to_bf16(y2);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
   // Q^T as the B operand: lane (row n, group kg) holds d = 32dc + 8kg + e.
   bf16x8 qf[NDC];
-  {
+  if (rope_q) {
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      qf[dc] = row_ok ? *reinterpret_cast<const bf16x8*>(q_rot + n * D + 32 * dc + 8 * kg)
+                      : as_bf16x8(u32x4{0, 0, 0, 0});
+  } else {
     const T* qr = reinterpret_cast<const T*>(p.q.data) + (int64_t)b * p.q.sB +
                   (int64_t)(row_ok ? head : 0) * p.q.sH + (int64_t)(row_ok ? qi : 0) * p.q.sS;
 #pragma unroll
@@ -219,29 +265,6 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       u32x4 v = {0, 0, 0, 0};
       if (row_ok) v = Load8<T>::load(qr + 32 * dc + 8 * kg);
       qf[dc] = as_bf16x8(v);
-    }
-    if constexpr (FUSED) {
-      // rotate-half RoPE of the raw query row at the new token's position:
-      // the lane holds d = 32 dc + 8 kg + e and its partner d + D/2 in
-      // register dc + NDC/2; the result is rounded to bf16 as stored q is
-      if (p.rope) {
-#pragma unroll
-        for (int dc = 0; dc < NDC / 2; ++dc) {
-          bf16x8 y1, y2;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 32 * dc + 8 * kg + e;
-            const float c = p.rc[j], sn = p.rs[j];
-            const float x1 = (float)qf[dc][e], x2 = (float)qf[dc + NDC / 2][e];
-            float r1, r2;
-            rope_rotate(x1, x2, c, sn, r1, r2);
-            y1[e] = (__bf16)r1;
-            y2[e] = (__bf16)r2;
-          }
-          qf[dc] = y1;
-          qf[dc + NDC / 2] = y2;
-        }
-      }
     }
   }
   f32x4 oacc[NDB];

@@ -156,7 +156,9 @@ __global__ __launch_bounds__(NW * 64) void flash_kernel(const FlashParams p) {
   auto issue_loads = [&](int t) {
     const bool A = t < nt0;
     const int64_t kt = tile_start(t);
-    const int64_t rows = A ? p.pk_rows : p.kv_rows;
+    // keys past the range end are zero-filled, never read: they may be
+    // unwritten memory (0 * NaN in the PV product would poison the output)
+    const int64_t rows = A ? ra1 : rb1;
     const T* kbs = A ? pkbase : kbase;
     const T* vbs = A ? pvbase : vbase;
     const int64_t kss = A ? p.pk.sS : p.k.sS;

@@ -124,25 +124,6 @@ __device__ __forceinline__ s16x4 tr_read(int addr) {
 #endif
 }
 
-// Rotate-half RoPE of this lane's Q fragments in place, at position pos:
-// the lane holds d = 16 dc + 8 hf + e, and its partner d + 64 sits in
-// fragment dc + 4.  Angle, sin/cos and rotation are the RoPE kernel's
-// (rope_math.h), then one rounding to bf16, so the rotated Q is bit for bit
-// the one star_rope_apply would store.
-__device__ __forceinline__ void rope_q(bf16x8* qf, double pos, int hf, const double* inv_freq) {
-#pragma unroll
-  for (int dc = 0; dc < 4; ++dc)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 16 * dc + e;
-      float cs, sn, y1, y2;
-      rope_angle(pos, hf ? inv_freq[j + 8] : inv_freq[j], cs, sn);
-      rope_rotate((float)qf[dc][e], (float)qf[dc + 4][e], cs, sn, y1, y2);
-      qf[dc][e] = (__bf16)y1;
-      qf[dc + 4][e] = (__bf16)y2;
-    }
-}
-
 // Dynamic item order (when the caller passes a scheduling workspace).  The
 // items are cut into 8 queues, queue x being the contiguous range the static
 // order gives XCD x (heavy first), and sched[x] counts the tickets handed out
@@ -180,24 +161,34 @@ __global__ void sched_reset_kernel(int32_t* sched) {
   if (threadIdx.x < STAR_SCHED_INTS) sched[threadIdx.x] = 0;
 }
 
-// Rotate-half RoPE of this lane's Q fragments from a cos/sin table in LDS:
-// (cos, sin) of position r (relative to the item's first row) and frequency
-// j at tab[j][r] (two floats), frequencies 0..31 in tlo, 32..63 in thi, NR
-// positions per frequency.  Same angles and rotation as rope_q.
-__device__ __forceinline__ void rope_q_tab(bf16x8* qf, int r, int hf, int NR, int tlo,
-                                           int thi) {
+// Rotate-half RoPE of this lane's Q fragments whose frequency falls in one
+// pass of a cos/sin table in LDS.  The lane holds d = 16 dc + 8 hf + e
+// (frequency j = d) in fragment dc and its partner d + 64 in fragment
+// dc + 4.  The pass covers frequencies [j0, j0 + FPP); the fp64 (cos, sin)
+// of position r (relative to the item's first row) and frequency j0 + i is
+// at tab(i, r) = (i < FPP/2 ? tlo : thi) + ((i mod FPP/2) NR + r) 16 bytes.
+// Angles and rotation are the RoPE kernel's (rope_math.h), then one
+// rounding to bf16, so the rotated Q is bit for bit the one
+// star_rope_apply would store.
+__device__ __forceinline__ void rope_q_pass(bf16x8* qf, int j0, int FPP, int r, int hf, int NR,
+                                            int tlo, int thi) {
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  const int half = FPP >> 1;
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc)
+  for (int dc = 0; dc < 4; ++dc) {
+    const int jb = 16 * dc + 8 * hf;              // this fragment's frequencies jb .. jb + 7
+    if (jb < j0 || jb >= j0 + FPP) continue;       // wave-uniform unless FPP = 8
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = 16 * dc + 8 * hf + e;
-      const int addr = (j < 32 ? tlo + j * NR * 8 : thi + (j - 32) * NR * 8) + r * 8;
-      const f32x2 cs = *lds_ptr<f32x2>(addr);
-      float y1, y2;
-      rope_rotate((float)qf[dc][e], (float)qf[dc + 4][e], cs.x, cs.y, y1, y2);
-      qf[dc][e] = (__bf16)y1;
-      qf[dc + 4][e] = (__bf16)y2;
+      const int i = jb + e - j0;
+      const int addr = (i < half ? tlo + i * NR * 16 : thi + (i - half) * NR * 16) + r * 16;
+      const f64x2 cs = *lds_ptr<f64x2>(addr);
+      double y1, y2;
+      rope_rotate64((double)(float)qf[dc][e], (double)(float)qf[dc + 4][e], cs.x, cs.y, y1, y2);
+      qf[dc][e] = f64_to_bf16(y1);
+      qf[dc + 4][e] = f64_to_bf16(y2);
     }
+  }
 }
 
 __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
@@ -286,8 +277,11 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
                        ((int64_t)it.b * p.k.sB + (int64_t)it.kvh * p.k.sH) * 2 + it.rb0 * ksB;
   const uint8_t* vbB = reinterpret_cast<const uint8_t*>(p.v.data) +
                        ((int64_t)it.b * p.v.sB + (int64_t)it.kvh * p.v.sH) * 2 + it.rb0 * vsB;
-  // rows of each range that stay inside its source tensor
-  const int64_t rowsA = p.pk_rows - it.ra0, rowsB = p.kv_rows - it.rb0;
+  // rows of each range (already clamped to its source tensor): a tile row
+  // past the range end re-reads the range's last row (masked later), so no
+  // row outside the range is ever read -- it may be unwritten memory, and
+  // 0 * NaN in the PV product would poison the output
+  const int64_t rowsA = it.ra1 - it.ra0, rowsB = it.rb1 - it.rb0;
   int lrow[2], lcolb[2];
   uint32_t okA[2], ovA[2], okB[2], ovB[2];
 #pragma unroll
@@ -307,9 +301,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // Tiles are loaded in order, range A's then range B's.  The loader keeps
   // the next tile's K and V row pointers (advanced by one 64-bit add per
   // tile), the strides and lane offsets of its range, the number of tiles
-  // left in the range and how many of them lie wholly inside the source
-  // tensor.  Rows past the source's end (last tile only) are clamped to its
-  // last row and masked later.
+  // left in the range and how many of them lie wholly inside the range.
+  // Rows past the range's end (last tile only) are clamped to its last row
+  // and masked later.
   const uint8_t* lk = kbA;
   const uint8_t* lv = vbA;
   int64_t lks = ksA, lvs = vsA, lrows = rowsA;
@@ -460,33 +454,44 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   if (nt > 1) load_next(1);
-  // RoPE of Q, under the tile loads.  With 4 or more query heads per
-  // workgroup, the workgroup's (at most 64) positions are shared by several
-  // waves: each (position, frequency) angle is then computed once, into the
-  // third tile slot (not loaded before the first barrier of the key loop),
-  // and read back by every wave of that position.
+  // RoPE of Q, under the tile loads.  The workgroup's NR = 32 npg positions
+  // (32 at g >= 5, 64 at g = 3, 4, up to 256 at g = 1) share each
+  // (position, frequency) cos/sin among its waves: it is computed once, in
+  // fp64, into a table in the third tile slot (32 KiB, not loaded before the
+  // first barrier of the key loop) and read back by every wave of that
+  // position.  The table of all 64 frequencies is 16 NR KiB, so it is built
+  // and used in passes of FPP = 2048 / NR frequencies.  A pass has 2048
+  // entries (i, r) = (frequency, position), entry e = i NR + r; wave w
+  // computes entries 256 w + 64 m + lane, m = 0..3.  The frequency of such
+  // an entry is wave-uniform for NR >= 64 and takes one of two values for
+  // NR = 32, so its loads are scalar ones and the compiler's wait for them
+  // does not also wait for the tile DMAs in flight.
   if (p.q_rope) {
-    if (p.gw >= 4) {
-      const int NR = 32 * p.npg;                    // 32 or 64 positions
-      const int tlo = (int)lds_u32(smK + 2 * TILE), thi = (int)lds_u32(smV + 2 * TILE);
-      // wave w: frequencies w, w + 8, ..., lane = position.  The frequency
-      // is wave-uniform, so its load is a scalar one and the compiler's
-      // wait for it does not also wait for the tile DMAs in flight.
-      if (lane < NR) {
-        const double pos = (double)(it.qr0 + lane + p.pos_shift);
-#pragma unroll 2
-        for (int k = 0; k < 8; ++k) {
-          const int j = wave + 8 * k;
-          float c, sn;
-          rope_angle(pos, p.inv_freq[j], c, sn);
-          const int addr = (j < 32 ? tlo + j * NR * 8 : thi + (j - 32) * NR * 8) + lane * 8;
-          *(__attribute__((address_space(3))) f32x2*)(uintptr_t)(uint32_t)addr = f32x2{c, sn};
-        }
+    typedef double f64x2 __attribute__((ext_vector_type(2)));
+    const int NR = 32 * p.npg;
+    const int FPP = 2048 / NR;
+    const int tlo = (int)lds_u32(smK + 2 * TILE), thi = (int)lds_u32(smV + 2 * TILE);
+    const int hi32 = (NR == 32) ? (lane >> 5) : 0;
+    for (int j0 = 0; j0 < D / 2; j0 += FPP) {
+      if (j0 > 0) __syncthreads();                  // every wave done with the last pass
+#pragma unroll 1
+      for (int m = 0; m < 4; ++m) {
+        const int e0 = 256 * wave + 64 * m;         // wave-uniform
+        const int i0 = e0 / NR, r0 = e0 - i0 * NR;
+        const double th0 = p.inv_freq[j0 + i0];
+        const double th1 = p.inv_freq[j0 + min(i0 + 1, FPP - 1)];
+        const double th = hi32 ? th1 : th0;
+        const int i = i0 + hi32;
+        const int r = (NR == 32) ? (lane & 31) : r0 + lane;
+        double c, sn;
+        rope_cs((double)(it.qr0 + r + p.pos_shift), th, c, sn);
+        const int addr = (i < (FPP >> 1) ? tlo + i * NR * 16 : thi + (i - (FPP >> 1)) * NR * 16) +
+                         r * 16;
+        *(__attribute__((address_space(3))) f64x2*)(uintptr_t)(uint32_t)addr = f64x2{c, sn};
       }
       __syncthreads();
-      rope_q_tab(qf, 32 * pg + l32, hf, NR, tlo, thi);
-    } else {
-      rope_q(qf, (double)qpos, hf, p.inv_freq);
+      // (a wave with no column block of its own has no rows to rotate)
+      if (cb_ok) rope_q_pass(qf, j0, FPP, 32 * pg + l32, hf, NR, tlo, thi);
     }
   }
   if (nt > 1) wait_vm_keep4(); else __builtin_amdgcn_s_waitcnt(0);

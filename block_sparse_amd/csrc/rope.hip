@@ -7,10 +7,11 @@
 // position ids preserve RoPE geometry).  Rotate-half form: pair (j, j+D/2)
 // turns by pos * theta_j.
 //
-// The angle and the rotation are in rope_math.h (fp64 angle reduction).
+// The angle, its cos/sin and the rotation are fp64 (rope_math.h), rounded
+// once to the output dtype.
 //
 // Both kernels are HBM-bound streams: a thread owns 8 pairs of one row
-// (two 16-byte loads for bf16), computes their sin/cos once and applies them
+// (two 16-byte loads for bf16), computes their cos/sin once and applies them
 // to every head of that position, so the trigonometry is amortised over H.
 #include "common.h"
 #include "internal.h"
@@ -41,19 +42,34 @@ __device__ __forceinline__ void load8<float>(const float* p, float* out) {
   }
 }
 
+// 8 fp64 values -> 8 stored elements, each rounded once (nearest even)
 template <typename T>
-__device__ __forceinline__ void store8(T* p, const float* in);
+__device__ __forceinline__ void store8(T* p, const double* in);
 template <>
-__device__ __forceinline__ void store8<__bf16>(__bf16* p, const float* in) {
+__device__ __forceinline__ void store8<__bf16>(__bf16* p, const double* in) {
   u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = pack_bf16(in[2 * i], in[2 * i + 1]);
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16_f64(in[2 * i], in[2 * i + 1]);
   *reinterpret_cast<u32x4*>(p) = w;
 }
 template <>
-__device__ __forceinline__ void store8<float>(float* p, const float* in) {
-  reinterpret_cast<f32x4*>(p)[0] = f32x4{in[0], in[1], in[2], in[3]};
-  reinterpret_cast<f32x4*>(p)[1] = f32x4{in[4], in[5], in[6], in[7]};
+__device__ __forceinline__ void store8<float>(float* p, const double* in) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{(float)in[0], (float)in[1], (float)in[2], (float)in[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{(float)in[4], (float)in[5], (float)in[6], (float)in[7]};
+}
+
+// rotate 8 pairs (x1[i], x2[i]) by the angles whose cos/sin are cs/sn
+__device__ __forceinline__ void rotate8(const float* x1, const float* x2, const double* cs,
+                                        const double* sn, double* y1, double* y2) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    rope_rotate64((double)x1[i], (double)x2[i], cs[i], sn[i], y1[i], y2[i]);
+}
+
+// copy 8 bf16 values through fp64 (exact both ways)
+__device__ __forceinline__ void widen8(const float* x, double* y) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (double)x[i];
 }
 
 // grid-stride over (head group, b, s, pair-chunk); loop over the heads of
@@ -75,21 +91,19 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeParams p, int hgrou
     const int hg = (int)(r / p.B);
     const int h0 = hg * hper, h1 = min(p.H, h0 + hper);
     const double pos = (double)(p.pos ? p.pos[s] : p.pos0 + s);
-    float cs[8], sn[8];
+    double cs[8], sn[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rope_angle(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
+    for (int i = 0; i < 8; ++i) rope_cs(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
     const T* xb = reinterpret_cast<const T*>(p.x.data) + (int64_t)b * p.x.sB + s * p.x.sS;
     T* yb = reinterpret_cast<T*>(p.y) + (int64_t)b * p.ysB + s * p.ysS;
     for (int h = h0; h < h1; ++h) {
       const T* xr = xb + (int64_t)h * p.x.sH;
       T* yr = yb + (int64_t)h * p.ysH;
-      float x1[8], x2[8], y1[8], y2[8];
+      float x1[8], x2[8];
+      double y1[8], y2[8];
       load8<T>(xr + 8 * ch, x1);
       load8<T>(xr + half + 8 * ch, x2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        rope_rotate(x1[i], x2[i], cs[i], sn[i], y1[i], y2[i]);
-      }
+      rotate8(x1, x2, cs, sn, y1, y2);
       store8<T>(yr + 8 * ch, y1);
       store8<T>(yr + half + 8 * ch, y2);
     }
@@ -119,23 +133,19 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
                  (p.slot0 + t) * p.vcsS;
     *reinterpret_cast<u32x4*>(vc + 8 * ch) = *reinterpret_cast<const u32x4*>(vr + 8 * ch);
     *reinterpret_cast<u32x4*>(vc + half + 8 * ch) = *reinterpret_cast<const u32x4*>(vr + half + 8 * ch);
-    float x1[8], x2[8], y1[8], y2[8];
+    float x1[8], x2[8];
+    double y1[8], y2[8];
     load8<__bf16>(kr + 8 * ch, x1);
     load8<__bf16>(kr + half + 8 * ch, x2);
     if (p.rope) {
       const double pos = (double)(p.pos0 + t);
+      double cs[8], sn[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float c, s;
-        rope_angle(pos, p.inv_freq[8 * ch + i], c, s);
-        rope_rotate(x1[i], x2[i], c, s, y1[i], y2[i]);
-      }
+      for (int i = 0; i < 8; ++i) rope_cs(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
+      rotate8(x1, x2, cs, sn, y1, y2);
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        y1[i] = x1[i];
-        y2[i] = x2[i];
-      }
+      widen8(x1, y1);
+      widen8(x2, y2);
     }
     store8<__bf16>(kc + 8 * ch, y1);
     store8<__bf16>(kc + half + 8 * ch, y2);
@@ -181,23 +191,19 @@ __global__ __launch_bounds__(256) void prepare_kernel(const PrepareParams pp) {
       *reinterpret_cast<u32x4*>(vc + half + 8 * ch) =
           *reinterpret_cast<const u32x4*>(vr + half + 8 * ch);
     }
-    float x1[8], x2[8], y1[8], y2[8];
+    float x1[8], x2[8];
+    double y1[8], y2[8];
     load8<__bf16>(src + 8 * ch, x1);
     load8<__bf16>(src + half + 8 * ch, x2);
     if (p.rope) {
       const double pos = (double)(p.pos0 + t);
+      double cs[8], sn[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float c, sn;
-        rope_angle(pos, p.inv_freq[8 * ch + i], c, sn);
-        rope_rotate(x1[i], x2[i], c, sn, y1[i], y2[i]);
-      }
+      for (int i = 0; i < 8; ++i) rope_cs(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
+      rotate8(x1, x2, cs, sn, y1, y2);
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        y1[i] = x1[i];
-        y2[i] = x2[i];
-      }
+      widen8(x1, y1);
+      widen8(x2, y2);
     }
     store8<__bf16>(dst + 8 * ch, y1);
     store8<__bf16>(dst + half + 8 * ch, y2);

@@ -102,9 +102,15 @@ typedef struct {
  * p * theta_j, theta_j = base^(-2j/D): the anchor block keeps the first
  * block's positions and every token keeps its own (Pith review of Star
  * Attention, "What carries the argument"; atlas.scime.ai summary, anchor
- * position-id ablation).  The angle is reduced in fp64 so that it stays
- * exact to about 1e-7 rad at million-token positions; sin/cos and the
- * rotation run in fp32; the result is rounded to the output dtype.
+ * position-id ablation).  Everything before the one rounding to the
+ * output dtype is fp64: the angle is the IEEE product p * theta_j (theta_j
+ * as star_rope_freqs returns it), cos/sin are fp64, the pair is rotated in
+ * fp64 and rounded once to nearest even.  The stored value is therefore the
+ * exact rotation of the input rounded once, up to fp64 rounding (it can
+ * differ only where that value lies within a few fp64 ulps of a rounding
+ * midpoint).  Every kernel that rotates (star_kv_append,
+ * star_decode_prepare, star_phase1_rope, star_decode_step) uses the same
+ * arithmetic, so they store the same bits for the same position.
  *
  *   x_in   [B, H, S, D] bf16 or fp32.
  *   x_out  same shape and dtype; may alias x_in exactly (in place).
@@ -114,6 +120,18 @@ typedef struct {
 int star_rope_apply(const star_tensor* x_in, const star_tensor* x_out,
                     const int64_t* pos, int64_t pos0, double base,
                     void* stream);
+
+/*
+ * The RoPE frequencies every rotating entry point uses (host only, no GPU
+ * call): inv_freq[j] = theta_j = base^(-2j/D) for j < D/2, evaluated in
+ * extended precision and rounded once to fp64 (the fp64 value nearest the
+ * exact power).
+ *   D         head dim: 16 <= D <= 128, D % 16 == 0 (else
+ *             STAR_ERR_UNSUPPORTED).
+ *   base      > 1 and finite (else STAR_ERR_SHAPE).
+ *   inv_freq  host double [D / 2] output (else STAR_ERR_NULL).
+ */
+int star_rope_freqs(int64_t D, double base, double* inv_freq);
 
 /*
  * Append new tokens' KV to a position-contiguous cache: the query host
@@ -307,13 +325,16 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
  * s_n = -inf carry no weight (Pith review of Star Attention, Referee Report
  * minor comment on Algorithm 2; "Circularity Check").
  *
- *   o_part    fp32 [N, R, D] contiguous, R = o->B * o->H * o->S.
- *   lse_part  fp32 [N, R] contiguous.
- *   o         [B, H, S, D] bf16 or fp32 output (row r = (b*H + h)*S + s).
- *   lse       fp32 [R] contiguous output, or NULL.
- * 1 <= N <= 65536.
+ *   o_part    fp32 [N, B, Hq, Lq, D] contiguous (star_phase2_partial's
+ *             layout; R = B * Hq * Lq rows per partial).
+ *   lse_part  fp32 [N, B, Hq, Lq] contiguous.
+ *   o         [B, Hq, Lq, D] bf16 or fp32 output, any strides; its sizes
+ *             must equal the B, Hq, Lq, D given (else STAR_ERR_SHAPE).
+ *   lse       fp32 [B, Hq, Lq] contiguous output, or NULL.
+ * 1 <= N <= 65536; D is 64 or 128.
  */
 int star_lse_merge(const float* o_part, const float* lse_part, int32_t N,
+                   int64_t B, int64_t Hq, int64_t Lq, int64_t D,
                    const star_tensor* o, float* lse, void* stream);
 
 /*
@@ -324,14 +345,19 @@ int star_lse_merge(const float* o_part, const float* lse_part, int32_t N,
  * launch -- followed by the star_lse_merge of those partials.  Each
  * generated token attends globally to every cached token (Pith review of
  * Star Attention, "What carries the argument", "Core claim" and
- * "Circularity Check").  The cos/sin of the token's angles are computed on
- * the host in fp64 and rounded once to fp32.
+ * "Circularity Check").  The rotation is star_rope_apply's (fp64, one
+ * rounding), so the appended K row equals star_kv_append's bit for bit.
+ * The cache is position-contiguous: the token's row is its position, so
+ * slot must equal pos (else STAR_ERR_SHAPE); it sees every cache row
+ * c <= pos of the partitions, including its own.
  *
  *   q_new             [B, Hq, 1, D] bf16, un-rotated.
  *   k_new, v_new      [B, Hkv, 1, D] bf16 (k un-rotated).
  *   k_cache, v_cache  [B, Hkv, S, D] bf16; row `slot` is overwritten.
  *   part_offsets      host int64 [P + 1] as for star_phase2_partial;
  *                     part_offsets[0] <= slot < part_offsets[P].
+ *                     Rows past slot are never read, so they may hold
+ *                     anything (unwritten cache rows).
  *   o_part, lse_part  device fp32 workspaces of star_phase2_partial's sizes
  *                     ([P*splits, B, Hq, 1, D] and [P*splits, B, Hq]);
  *                     they hold the chunk partials afterwards.

@@ -1,9 +1,25 @@
 """Helpers shared by the GPU parity tests (not collected by pytest).
 
 Tolerances (from the method's numeric contract: bf16 in, fp32 accumulate):
-attention outputs max-abs <= 1e-2 (plus, for outputs stored in bf16, the
-bf16 rounding of the value itself) and mean-abs <= 1e-3, log-sum-exp values
-|d| <= 1e-3, and no NaN/Inf anywhere.
+attention outputs max-abs <= 1e-2 and mean-abs <= 1e-3 against the exact
+result, log-sum-exp values |d| <= 1e-3, and no NaN/Inf anywhere.
+
+An output stored in bf16 (Phase-1 O, layer outputs) may exceed 1e-2 only
+where bf16 itself cannot do better: its element bound is
+max(1e-2, 2^-8 |ref| + c), where 2^-8 |ref| is the value's own rounding to
+bf16 (half an ulp) and c the compute error the kernel's arithmetic admits:
+  * attention (``wabs`` given): c = 2^-9 wabs + 1e-4.  The kernel rounds each
+    softmax weight to bf16 for the PV product (relative error 2^-9), which
+    moves an output element by at most 2^-9 sum_i w_i |V_i,d| = 2^-9 wabs,
+    the softmax average of |V| (the oracle's output for |V|); 1e-4 covers the
+    fp32 accumulation.  For rows that see many keys c ~ 1e-3, so the bound is
+    1e-2; it exceeds 1e-2 only in rows dominated by a few large values.
+  * projections and layer outputs (``layer=True``), checked against the
+    oracle fed the stage's actual bf16 input: c = LAYER_C = 1e-4, the fp32
+    accumulation of a GEMM with K <= 4096 terms of unit-scale products.
+The mean is taken against the exact result, except for the layer stages: a
+unit-scale value rounded to bf16 alone is off by ~1.05e-3 on average, so
+those are compared with the exact result rounded to bf16.
 """
 import math
 
@@ -39,25 +55,37 @@ def rand_tensor(seed, tid, B, H, S, D, scale=1.0, bf16=True):
     return draw_tensor(seed, tid, B, H, S, D, scale, as_bf16=bf16)
 
 
+LAYER_C = 1e-4
+
+
 def check_out(got: np.ndarray, ref: np.ndarray, what: str,
-              max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS, bf16_out=False):
-    """Element-wise max-abs and overall mean-abs bounds.  For a bf16 output
-    (Phase-1 O, layer outputs) the bound on an element also admits the
-    rounding of that output to bf16, at most 2^-8 |ref| (half an ulp,
-    relative to the value): a stored bf16 value of magnitude above ~2.5
-    cannot be within 1e-2 of the exact result; and the mean is taken
-    against the exact result rounded to bf16."""
+              max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS, bf16_out=False, wabs=None,
+              layer=False):
+    """Element-wise max-abs and overall mean-abs bounds (see the module
+    docstring).  ``bf16_out``: the output is stored in bf16; then either
+    ``wabs`` (the softmax average of |V| for every output element) or
+    ``layer=True`` states the compute term."""
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = np.abs(got - ref)
-    lim = max_abs + (2.0 ** -8) * np.abs(ref) if bf16_out else max_abs
+    if bf16_out:
+        if layer:
+            c = LAYER_C
+        else:
+            assert wabs is not None and wabs.shape == ref.shape, f"{what}: wabs needed"
+            c = 2.0 ** -9 * wabs + 1e-4
+        lim = np.maximum(max_abs, (2.0 ** -8) * np.abs(ref) + c)
+    else:
+        lim = max_abs
     mx = float(err.max(initial=0.0))
-    # the mean is taken against the exact value as the output dtype stores
-    # it: rounding unit-scale values to bf16 alone costs ~1e-3 on average
-    merr = np.abs(got - round_bf16(ref)) if bf16_out else err
+    merr = np.abs(got - round_bf16(ref)) if (bf16_out and layer) else err
     mn = float(merr.mean()) if merr.size else 0.0
-    ok = bool((err <= lim).all())
-    assert ok and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+    bad = err > lim
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(err - lim)), err.shape)
+        raise AssertionError(f"{what}: max-abs {mx:.3e} over the bound at {i}: got {got[i]!r} "
+                             f"ref {ref[i]!r} bound {np.broadcast_to(lim, err.shape)[i]:.3e}")
+    assert mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
     return mx, mn
 
 
@@ -86,3 +114,16 @@ def chunk_ranges(part_offsets, splits, align=64):
             lo = a + s * c
             out.append((min(lo, b), max(min(lo + c, b), min(lo, b))))
     return out
+
+
+def with_wabs(fn, V, *args, v_index: int):
+    """Run a row-wise oracle function whose values argument (position
+    ``v_index`` in ``args``) is ``V`` on [V | |V|] (the value width follows
+    V's), returning ``(o, lse, wabs)``: the output for V and, from the same
+    softmax weights, their average of |V| (the compute term of a bf16
+    output's bound)."""
+    D = V.shape[-1]
+    a = list(args)
+    a.insert(v_index, np.concatenate([V, np.abs(V)], axis=-1))
+    o, l = fn(*a)
+    return o[..., :D], l, o[..., D:]

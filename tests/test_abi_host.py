@@ -12,9 +12,6 @@ from block_sparse_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "star_attn.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
-                                reason="libstarattn.so not built")
-
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced on the host
 
 
@@ -31,6 +28,11 @@ def T(B=1, H=2, S=64, D=64, dtype=0, data=FAKE, strides=None):
 
 @pytest.fixture(scope="module")
 def lib():
+    """The built library; built here (hipcc cross-compiles without a GPU)
+    when it is missing, and a failed build fails the tests."""
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_amd import build
+        build.build()
     return _lib.load()
 
 
@@ -39,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 300
+    assert lib.star_abi_version() == 400
 
 
 def test_status_strings(lib):
@@ -132,13 +134,21 @@ def test_phase2_validation(lib):
 
 def test_merge_rope_append_validation(lib):
     o = T(B=1, H=2, S=4, D=64)
-    m = lambda n, oo=o, op=FAKE, lp=FAKE: lib.star_lse_merge(op, lp, n, ctypes.byref(oo), None, None)
+
+    def m(n, oo=o, op=FAKE, lp=FAKE, shape=None):
+        B, H, S, D = shape or (oo.B, oo.H, oo.S, oo.D)
+        return lib.star_lse_merge(op, lp, n, B, H, S, D, ctypes.byref(oo), None, None)
     assert m(1, op=None) == -1
     assert m(0) == -2
     assert m(70000) == -2
     assert m(2, oo=T(B=1, H=2, S=4, D=80)) == -5
     assert m(2, op=FAKE + 8) == -4
     assert m(2, oo=T(B=1, H=2, S=0, D=64)) == 0
+    # the sizes given must be the output's
+    assert m(2, shape=(2, 2, 4, 64)) == -2
+    assert m(2, shape=(1, 1, 4, 64)) == -2
+    assert m(2, shape=(1, 2, 5, 64)) == -2
+    assert m(2, shape=(1, 2, 4, 128)) == -2
     x = T(B=1, H=2, S=8, D=128)
     r = lambda a, b, pos=None, pos0=0, base=5e5: lib.star_rope_apply(
         ctypes.byref(a), ctypes.byref(b), pos, pos0, base, None)
@@ -289,9 +299,12 @@ def test_decode_step_validation(lib):
                                     ctypes.byref(kc), ctypes.byref(vc), slot, pos, base, rope,
                                     arr, len(offs) - 1, splits, 0.1, op, lp, ctypes.byref(oo),
                                     None, None)
-    assert ds(slot=51) == -2                       # slot outside the partitions
-    assert ds(slot=-1) == -2
+    assert ds(slot=51, pos=51) == -2               # slot outside the partitions
+    assert ds(slot=-1, pos=-1) == -2
     assert ds(pos=-1) == -2
+    # the cache is position-contiguous: the token's row is its position
+    assert ds(slot=49, pos=50) == -2
+    assert ds(slot=50, pos=49) == -2
     assert ds(q=T(B=1, H=8, S=2, D=128)) == -2     # one token per call
     assert ds(k=T(B=1, H=2, S=1, D=64)) == -2
     assert ds(oo=T(B=1, H=8, S=2, D=128)) == -2
@@ -302,3 +315,21 @@ def test_decode_step_validation(lib):
     assert ds(offs=(0, 40, 101)) == -2
     assert ds(base=1.0) == -2
     assert ds(splits=0) == -2
+
+
+def test_rope_freqs_are_the_nearest_float64(lib):
+    """The frequencies every rotating kernel uses equal the oracle's (the
+    float64 nearest base^(-2j/D), from decimal arithmetic) bit for bit, at
+    every head dim the RoPE entry points accept and several bases."""
+    import oracle.star_oracle as so
+    for base in (100.0, 10000.0, 500000.0, 1e6, 1234567.0):
+        for D in range(16, 129, 16):
+            out = (ctypes.c_double * (D // 2))()
+            assert lib.star_rope_freqs(D, base, out) == 0
+            assert list(out) == so.rope_theta(D, base).tolist(), (base, D)
+    out = (ctypes.c_double * 64)()
+    assert lib.star_rope_freqs(128, 5e5, None) == -1
+    assert lib.star_rope_freqs(72, 5e5, out) == -5
+    assert lib.star_rope_freqs(8, 5e5, out) == -5
+    assert lib.star_rope_freqs(128, 1.0, out) == -2
+    assert lib.star_rope_freqs(128, float("inf"), out) == -2

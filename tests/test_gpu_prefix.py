@@ -56,7 +56,9 @@ def test_phase1_prefix_parity(case):
     torch.cuda.synchronize()
     ref_o, ref_l = so.phase1_prefix(f64(q), f64(k), f64(v), f64(pk), f64(pv), st, ln, b,
                                     1 / math.sqrt(D))
-    check_out(host64(o), ref_o, "O", bf16_out=True)
+    wabs, _ = so.phase1_prefix(f64(q), f64(k), np.abs(f64(v)), f64(pk), np.abs(f64(pv)), st, ln,
+                               b, 1 / math.sqrt(D))
+    check_out(host64(o), ref_o, "O", bf16_out=True, wabs=wabs)
     check_lse(host64(lse), ref_l, "LSE")
 
 
@@ -112,9 +114,10 @@ def test_anchor_at_other_positions_parity():
     K = so.round_bf16(so.rope(f64(k), P, st.base))
     PK = so.remapped_anchor(f64(k), pos, st.base)
     PV = np.concatenate([f64(v)[..., :b, :]] * len(pos), axis=-2)
-    ref_o, ref_l = so.phase1_prefix(Q, K, f64(v), PK, PV, np.arange(len(pos)) * b,
-                                    [0] + [b] * (len(pos) - 1), b, 1 / math.sqrt(D))
-    check_out(host64(st.o1), ref_o, "O", bf16_out=True)
+    tab = (np.arange(len(pos)) * b, [0] + [b] * (len(pos) - 1))
+    ref_o, ref_l = so.phase1_prefix(Q, K, f64(v), PK, PV, *tab, b, 1 / math.sqrt(D))
+    wabs, _ = so.phase1_prefix(Q, K, np.abs(f64(v)), PK, np.abs(PV), *tab, b, 1 / math.sqrt(D))
+    check_out(host64(st.o1), ref_o, "O", bf16_out=True, wabs=wabs)
     check_lse(host64(st.lse1), ref_l, "LSE")
 
 
@@ -143,5 +146,8 @@ def test_pulsar_phase1_parity(B, L, b, k):
         ref_o, ref_l = so.phase1_prefix(Q[bb:bb + 1], K[bb:bb + 1], V[bb:bb + 1],
                                         K[bb:bb + 1][:, :, rows], V[bb:bb + 1][:, :, rows],
                                         s0, l0, b, 1 / math.sqrt(D))
-        check_out(host64(st.o1[bb:bb + 1]), ref_o, f"O b={bb}", bf16_out=True)
+        Va = np.abs(V[bb:bb + 1])
+        wabs, _ = so.phase1_prefix(Q[bb:bb + 1], K[bb:bb + 1], Va, K[bb:bb + 1][:, :, rows],
+                                   Va[:, :, rows], s0, l0, b, 1 / math.sqrt(D))
+        check_out(host64(st.o1[bb:bb + 1]), ref_o, f"O b={bb}", bf16_out=True, wabs=wabs)
         check_lse(host64(st.lse1[bb:bb + 1]), ref_l, f"LSE b={bb}")

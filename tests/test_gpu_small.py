@@ -10,7 +10,7 @@ import torch
 import block_sparse_amd as sa
 import oracle.star_oracle as so
 from gpu_util import (check_lse, check_out, chunk_ranges, f64, host64, rand_tensor,
-                      to_dev)
+                      to_dev, with_wabs)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,8 @@ def test_phase1_parity(case):
     o, lse = sa.phase1_blocklocal(to_dev(q), to_dev(k), to_dev(v), b, a, want_lse=True)
     torch.cuda.synchronize()
     ref_o, ref_l = so.phase1(f64(q), f64(k), f64(v), b, a if b < L else 0, scale)
-    check_out(host64(o), ref_o, "O", bf16_out=True)
+    wabs, _ = so.phase1(f64(q), f64(k), np.abs(f64(v)), b, a if b < L else 0, scale)
+    check_out(host64(o), ref_o, "O", bf16_out=True, wabs=wabs)
     check_lse(host64(lse), ref_l, "LSE")
 
 
@@ -84,9 +85,10 @@ def test_phase1_rope_parity(case):
     torch.cuda.synchronize()
     q_rot = so.round_bf16(so.rope(f64(q), pos, base))
     ref_o, ref_l = so.phase1(q_rot, k_rot, f64(v), b, a if b < L else 0, scale)
-    check_out(host64(o), ref_o, "O (fused rope)", bf16_out=True)
+    wabs, _ = so.phase1(q_rot, k_rot, np.abs(f64(v)), b, a if b < L else 0, scale)
+    check_out(host64(o), ref_o, "O (fused rope)", bf16_out=True, wabs=wabs)
     check_lse(host64(lse), ref_l, "LSE (fused rope)")
-    check_out(host64(o2), ref_o, "O (two passes)", bf16_out=True)
+    check_out(host64(o2), ref_o, "O (two passes)", bf16_out=True, wabs=wabs)
     check_lse(host64(lse2), ref_l, "LSE (two passes)")
     # the in-kernel rotation is the RoPE kernel's, bit for bit
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
@@ -175,7 +177,8 @@ def test_phase1_rescale_stress(case):
     o, lse = sa.phase1_blocklocal(dev(q), dev(k), dev(v), b, a, want_lse=True)
     torch.cuda.synchronize()
     ref_o, ref_l = so.phase1(q, k, v, b, a, scale)
-    check_out(host64(o), ref_o, "O", bf16_out=True)
+    wabs, _ = so.phase1(q, k, np.abs(v), b, a, scale)
+    check_out(host64(o), ref_o, "O", bf16_out=True, wabs=wabs)
     check_lse(host64(lse), ref_l, "LSE")
 
 
@@ -274,36 +277,64 @@ def test_merge_parity(N, D, out_bf16):
     check_lse(host64(l), ref_l, "merged LSE")
 
 
-@pytest.mark.parametrize("D,f32,pos0", [(128, False, 0), (128, False, 131000),
-                                        (64, True, 1048000), (128, True, 1048570)])
-def test_rope_parity(D, f32, pos0):
-    B, H, S = 2, 3, 67
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Bit patterns of a device tensor (uint16 for bf16, uint32 for fp32)."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def rot_bits(x64: np.ndarray, pos, base: float, f32: bool) -> np.ndarray:
+    """The oracle's exact rotation rounded once to the stored dtype, as bits."""
+    r = so.rope(x64, np.asarray(pos), base)
+    if f32:
+        return r.astype(np.float32).view(np.uint32)           # one RNE rounding
+    return so.round_bf16(r).astype(np.float32).view(np.uint32) >> 16
+
+
+def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
+    bad = np.nonzero(got != ref)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} elements differ, first at {list(zip(*bad))[:6]}"
+
+
+ROPE_BIT_CASES = [
+    # D, f32, positions
+    (128, False, np.arange(0, 4096)),                          # block starts, small angles
+    (128, False, np.arange(131072 - 2048, 131072 + 192)),      # the 128K context end
+    (128, False, np.arange(1048576 - 64, 1048576 + 64)),       # around 2^20
+    (128, True, np.arange(1048576 - 64, 1048576 + 64)),
+    (64, False, np.sort(np.random.default_rng(3).choice(2 ** 21, 3000, replace=False))),
+    (16, True, np.arange(0, 300) * 7919),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_BIT_CASES, ids=[str(i) for i in range(len(ROPE_BIT_CASES))])
+def test_rope_bit_exact(case):
+    """star_rope_apply stores the exact rotation rounded once (nearest even)
+    to the tensor's dtype: the same bits as the oracle's fp64 rotation
+    rounded once, over context, query and million-token positions, with a
+    contiguous range and with a position list."""
+    D, f32, pos = case
+    base = 500000.0
+    B, H, S = 2, 8, pos.size
     x = rand_tensor(31, 0, B, H, S, D, bf16=not f32)
     xd = to_dev(x)
-    out = sa.rope_apply(xd.clone(), pos0=pos0, base=500000.0)
-    pos = torch.arange(pos0, pos0 + S, dtype=torch.int64, device="cuda")
-    out2 = torch.empty_like(xd)
-    sa.rope_apply(xd, pos=pos, base=500000.0, out=out2)
+    contiguous = bool(np.all(np.diff(pos) == 1))
+    out1 = sa.rope_apply(xd, pos0=int(pos[0]), base=base, out=torch.empty_like(xd)) \
+        if contiguous else None
+    out2 = sa.rope_apply(xd, pos=torch.from_numpy(pos).cuda(), base=base,
+                         out=torch.empty_like(xd))
     torch.cuda.synchronize()
-    ref = so.rope(f64(x), np.arange(pos0, pos0 + S), 500000.0)
-    for got in (host64(out), host64(out2)):
-        err = np.abs(got - ref)
-        if f32:
-            assert err.max() < 2e-5, err.max()
-        else:  # bf16 rounding of the result: half an ulp, relative 2^-8
-            assert (err <= np.abs(ref) * 2.0**-8 + 1e-5).all(), err.max()
+    ref = rot_bits(f64(x), pos, base, f32)
+    for o in (out1, out2):
+        if o is not None:
+            got = bits(o).astype(np.uint32)
+            assert_bits_equal(got, ref, f"rope D={D} f32={f32}")
 
 
-def test_rope_angle_precision_at_1m():
-    """Unit pairs rotated at positions near 2^20: the fp32 result must sit
-    within ~1e-6 of (cos, sin) of the exact angle."""
-    D, S, pos0 = 128, 64, 1048576 - 64
-    x = np.zeros((1, 1, S, D), np.float32)
-    x[..., : D // 2] = 1.0
-    out = sa.rope_apply(to_dev(x), pos0=pos0, base=500000.0)
-    torch.cuda.synchronize()
-    ref = so.rope(x.astype(np.float64), np.arange(pos0, pos0 + S), 500000.0)
-    assert np.abs(host64(out) - ref).max() < 2e-6
+def test_rope_freqs_match_the_oracle():
+    for D in (16, 64, 128):
+        assert sa.rope_freqs(D, 500000.0) == so.rope_theta(D, 500000.0).tolist()
 
 
 def test_kv_append_parity():
@@ -314,17 +345,17 @@ def test_kv_append_parity():
     vc = torch.zeros_like(kc)
     sa.kv_append(to_dev(kn), to_dev(vn), kc, vc, slot0=30, pos0=123456, base=500000.0)
     torch.cuda.synchronize()
-    ref_k = so.rope(f64(kn), 123456 + np.arange(T), 500000.0)
-    got_k = host64(kc)[:, :, 30:35]
-    assert (np.abs(got_k - ref_k) <= np.abs(ref_k) * 2.0**-8 + 1e-5).all()
+    got = bits(kc).astype(np.uint32)
+    assert_bits_equal(got[:, :, 30:35], rot_bits(f64(kn), 123456 + np.arange(T), 500000.0, False),
+                      "appended K")
     assert np.array_equal(host64(vc)[:, :, 30:35], f64(vn))
     assert (host64(kc)[:, :, :30] == 0).all() and (host64(kc)[:, :, 35:] == 0).all()
 
 
 @pytest.mark.parametrize("rope", [True, False])
 def test_decode_prepare_parity(rope):
-    """rope(q) + KV append in one launch equals the oracle rotation (bf16
-    rounding of the result) and leaves the rest of the cache untouched."""
+    """rope(q) + KV append in one launch stores the oracle's rotation rounded
+    once, bit for bit, and leaves the rest of the cache untouched."""
     B, Hq, Hkv, T, D, S = 2, 8, 2, 3, 128, 50
     qn = rand_tensor(43, 6, B, Hq, T, D)
     kn = rand_tensor(43, 7, B, Hkv, T, D)
@@ -337,10 +368,13 @@ def test_decode_prepare_parity(rope):
                       base=500000.0, rope=rope)
     torch.cuda.synchronize()
     pos = pos0 + np.arange(T)
-    rq = so.rope(f64(qn), pos, 500000.0) if rope else f64(qn)
-    rk = so.rope(f64(kn), pos, 500000.0) if rope else f64(kn)
-    for got, ref in ((host64(qo), rq), (host64(kc)[:, :, 40:43], rk)):
-        assert (np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-5).all()
+    if rope:
+        assert_bits_equal(bits(qo).astype(np.uint32), rot_bits(f64(qn), pos, 500000.0, False), "q")
+        assert_bits_equal(bits(kc).astype(np.uint32)[:, :, 40:43],
+                          rot_bits(f64(kn), pos, 500000.0, False), "k")
+    else:
+        assert np.array_equal(host64(qo), f64(qn))
+        assert np.array_equal(host64(kc)[:, :, 40:43], f64(kn))
     assert np.array_equal(host64(vc)[:, :, 40:43], f64(vn))
     assert (host64(kc)[:, :, :40] == 0).all() and (host64(kc)[:, :, 43:] == 0).all()
 
@@ -387,9 +421,10 @@ def test_decode_step_parity(case):
     rot = (lambda x, p: so.round_bf16(so.rope(x, p, base))) if rope else (lambda x, p: x)
     K = np.concatenate([rot(f64(k), pos_c), rot(f64(kd), pos_d)], axis=2)
     V = np.concatenate([f64(v), f64(vd)], axis=2)
-    # the appended rows: rotated k (bf16 rounding of the exact rotation) and v
-    got_k = kc_f[:, :, L:L + T]
-    assert (np.abs(got_k - K[:, :, L:]) <= np.abs(K[:, :, L:]) * 2.0**-8 + 1e-5).all()
+    # the appended rows: rotated k (the exact rotation rounded once, the same
+    # bits on the fused and unfused paths) and v
+    assert np.array_equal(kc_f[:, :, L:L + T], K[:, :, L:])
+    assert np.array_equal(kc_u[:, :, L:L + T], K[:, :, L:])
     assert np.array_equal(vc_f[:, :, L:L + T], f64(vd))
     Qd = rot(f64(qd), pos_d)
     ref_o = np.zeros((B, Hq, T, D))
@@ -419,9 +454,9 @@ def test_phase1_many_small_blocks():
     pos = np.concatenate([np.arange(0, 48), np.arange(5000, 5040), np.arange(L - 40, L)])
     for h in (0, 5):
         qq = f64(q)[0, h][pos]
-        ro, rl = so.phase1_rows(qq, pos, f64(k)[0, h // 4], f64(v)[0, h // 4], b, b,
-                                1 / math.sqrt(D))
-        check_out(host64(o)[0, h][pos], ro, "O", bf16_out=True)
+        ro, rl, wabs = with_wabs(so.phase1_rows, f64(v)[0, h // 4], qq, pos, f64(k)[0, h // 4],
+                                 b, b, 1 / math.sqrt(D), v_index=3)
+        check_out(host64(o)[0, h][pos], ro, "O", bf16_out=True, wabs=wabs)
         check_lse(host64(lse)[0, h][pos], rl, "LSE")
 
 
@@ -441,7 +476,9 @@ def test_phase1_prefix_at_the_block_limit():
     torch.cuda.synchronize()
     ref_o, ref_l = so.phase1_prefix(f64(q), f64(k), f64(v), f64(pk), f64(pv), st, ln, b,
                                     1 / math.sqrt(D))
-    check_out(host64(o), ref_o, "O", bf16_out=True)
+    wabs, _ = so.phase1_prefix(f64(q), f64(k), np.abs(f64(v)), f64(pk), np.abs(f64(pv)), st, ln,
+                               b, 1 / math.sqrt(D))
+    check_out(host64(o), ref_o, "O", bf16_out=True, wabs=wabs)
     check_lse(host64(lse), ref_l, "LSE")
     with pytest.raises(sa.StarError):                   # 133 blocks: refused before any launch
         sa.phase1_prefix(to_dev(q), to_dev(k), to_dev(v), to_dev(pk), to_dev(pv),
