@@ -428,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c2, -msub));
-      ls += pv;
+      ls = e == 0 ? pv : ls + pv;          // (0 + pv would cost an add)
       pf[e >> 3][e & 7] = (__bf16)pv;
     }
     return ls;
@@ -566,19 +566,24 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     s = sn;
   };
 
-  for (int j = 0; j < nsub; j += 6) {
+  // whole 6-sub-tile cycles without an exit in the middle (an exit there
+  // makes the compiler materialise the dead loop state of the exit path in
+  // every step, stalling on the last MFMA's result), then the remainder
+  const int ncyc = nsub / 6, rem = nsub - 6 * ncyc;
+  int j = 0;
+  for (int c = 0; c < ncyc; ++c, j += 6) {
     step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 >= nsub) break;
     step(std::integral_constant<int, 1>{}, j + 1);
-    if (j + 2 >= nsub) break;
     step(std::integral_constant<int, 2>{}, j + 2);
-    if (j + 3 >= nsub) break;
     step(std::integral_constant<int, 3>{}, j + 3);
-    if (j + 4 >= nsub) break;
     step(std::integral_constant<int, 4>{}, j + 4);
-    if (j + 5 >= nsub) break;
     step(std::integral_constant<int, 5>{}, j + 5);
   }
+  if (rem > 0) step(std::integral_constant<int, 0>{}, j);
+  if (rem > 1) step(std::integral_constant<int, 1>{}, j + 1);
+  if (rem > 2) step(std::integral_constant<int, 2>{}, j + 2);
+  if (rem > 3) step(std::integral_constant<int, 3>{}, j + 3);
+  if (rem > 4) step(std::integral_constant<int, 4>{}, j + 4);
 
   // ---- epilogue
   const float lt = lsum + __shfl_xor(lsum, 32);
