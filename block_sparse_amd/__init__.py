@@ -24,6 +24,7 @@ from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 __all__ = ["rope_apply", "rope_freqs", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
            "phase1_prefix", "sched_workspace", "SCHED_INTS",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
+           "decode_step_noalloc",
            "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
            "StarError", "library"]
 
@@ -360,6 +361,30 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, slot: int, pos: int, part
                                     float(scale), _ptr(o_part), _ptr(lse_part),
                                     ctypes.byref(do), _ptr(lse), _stream(q_new))
     _lib.check("star_decode_step", st)
+    return out, lse
+
+
+def decode_step_noalloc(q_new, k_new, v_new, k_cache, v_cache, slot: int, pos: int,
+                        part_offsets, splits: int, out, lse=None, base: float = 500000.0,
+                        rope: bool = True, scale: float | None = None):
+    """:func:`decode_step` without caller workspaces: the partials live in the
+    library's per-GPU scratch array (star_decode_step_noalloc; nothing is
+    allocated).  Calls that may overlap on one GPU must not be issued."""
+    B, Hq, _, D = q_new.shape
+    P = len(part_offsets) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq] tensor")
+    offs = (ctypes.c_int64 * (P + 1))(*[int(x) for x in part_offsets])
+    d = [_desc(t) for t in (q_new, k_new, v_new, k_cache, v_cache)]
+    do = _desc(out)
+    st = library().star_decode_step_noalloc(*[ctypes.byref(x) for x in d], int(slot), int(pos),
+                                            float(base), int(bool(rope)), offs, int(P),
+                                            int(splits), float(scale), ctypes.byref(do),
+                                            _ptr(lse), _stream(q_new))
+    _lib.check("star_decode_step_noalloc", st)
     return out, lse
 
 

@@ -16,6 +16,7 @@ STAR_BF16 = 0
 STAR_F32 = 1
 STAR_MAX_PARTS = 128
 STAR_SPLIT_ALIGN = 64
+STAR_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 STATUS = {
     0: "STAR_OK", -1: "STAR_ERR_NULL", -2: "STAR_ERR_SHAPE", -3: "STAR_ERR_DTYPE",
@@ -27,6 +28,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("star_rope_apply", "star_rope_freqs", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase1_prefix", "star_phase1_rope", "star_gather_rows", "star_stream_read", "star_pulsar_prefix",
            "star_phase2_partial", "star_lse_merge", "star_decode_step",
+           "star_decode_step_noalloc",
            "star_context_create", "star_context_destroy", "star_rmsnorm", "star_linear",
            "star_status_string",
            "star_abi_version")
@@ -67,6 +69,8 @@ _SIGS = {
     "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _i64, _T, _vp, _vp]),
     "star_decode_step": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _P(_i64), _i32,
                                         _i32, _f32, _vp, _vp, _T, _vp, _vp]),
+    "star_decode_step_noalloc": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32,
+                                                _P(_i64), _i32, _i32, _f32, _T, _vp, _vp]),
     "star_context_create": (ctypes.c_int, [_P(_vp)]),
     "star_context_destroy": (ctypes.c_int, [_vp]),
     "star_rmsnorm": (ctypes.c_int, [_T, _vp, _f32, _T, _vp]),

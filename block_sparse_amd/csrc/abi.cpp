@@ -460,19 +460,26 @@ int star_phase2_partial(const star_tensor* q, const star_tensor* k_cache,
   return hip_status(star::launch_flash(p, (hipStream_t)stream));
 }
 
-int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
+}  // extern "C"
+
+namespace star {
+
+// star_decode_step's validation and launches.  With ws_given == false the
+// workspace pointers are not checked and nothing is launched (the no-alloc
+// entry point validates its arguments before it looks up its scratch).
+int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
                      const star_tensor* v_new, const star_tensor* k_cache,
                      const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
                      int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
                      float scale, float* o_part, float* lse_part, const star_tensor* o,
-                     float* lse, void* stream) {
+                     float* lse, void* stream, bool ws_given) {
   int s;
   if ((s = check_qkv(q_new, k_cache, v_cache)) != STAR_OK) return s;
   if ((s = check_tensor(k_new, false)) != STAR_OK) return s;
   if ((s = check_tensor(v_new, false)) != STAR_OK) return s;
   if ((s = check_tensor(o, true)) != STAR_OK) return s;
   if (q_new->dtype != STAR_BF16) return STAR_ERR_DTYPE;
-  if (o_part == nullptr || lse_part == nullptr) return STAR_ERR_NULL;
+  if (ws_given && (o_part == nullptr || lse_part == nullptr)) return STAR_ERR_NULL;
   if (q_new->S != 1 || k_new->S != 1 || v_new->S != 1) return STAR_ERR_SHAPE;
   for (const star_tensor* t : {k_new, v_new})
     if (t->B != k_cache->B || t->H != k_cache->H || t->D != k_cache->D) return STAR_ERR_SHAPE;
@@ -483,9 +490,9 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
   if (slot != pos || slot < part_offsets[0] || slot >= part_offsets[P]) return STAR_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
   if (rope && !(std::isfinite(base) && base > 1.0)) return STAR_ERR_SHAPE;
-  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
-      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return STAR_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return STAR_ERR_ALIGN;
+  if (!ws_given) return STAR_OK;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return STAR_ERR_ALIGN;
   star::DecodeParams p;
   decode_params(p, q_new, k_cache, v_cache, part_offsets, P, splits, chunk, pos, scale, o_part,
                 lse_part);
@@ -514,6 +521,21 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
   m.osS = o->sS;
   m.lse = lse;
   return hip_status(star::launch_merge(m, (hipStream_t)stream));
+}
+
+}  // namespace star
+
+extern "C" {
+
+int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
+                     const star_tensor* v_new, const star_tensor* k_cache,
+                     const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
+                     int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
+                     float scale, float* o_part, float* lse_part, const star_tensor* o,
+                     float* lse, void* stream) {
+  return star::decode_step_impl(q_new, k_new, v_new, k_cache, v_cache, slot, pos, base, rope,
+                                part_offsets, P, splits, scale, o_part, lse_part, o, lse, stream,
+                                true);
 }
 
 int star_rmsnorm(const star_tensor* x, const void* gamma, float eps, const star_tensor* y,

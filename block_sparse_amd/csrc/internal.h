@@ -91,6 +91,16 @@ struct DecodeParams {
 bool decode_supported(int g, int64_t Lq, int D);
 hipError_t launch_decode(DecodeParams& p, hipStream_t stream);
 
+// star_decode_step (abi.cpp): validation, then the fused decode launch and
+// the merge; ws_given == false validates everything but the workspaces and
+// launches nothing
+int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
+                     const star_tensor* v_new, const star_tensor* k_cache,
+                     const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
+                     int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
+                     float scale, float* o_part, float* lse_part, const star_tensor* o,
+                     float* lse, void* stream, bool ws_given);
+
 struct RopeParams {
   TensorRef x;
   void* y;

@@ -37,8 +37,9 @@
  *   star_linear runs rocBLAS, which manages its own device workspace (it
  *   may allocate it on a first call).  Work is enqueued on `stream` (a
  *   hipStream_t passed as void*; NULL = the null stream) and the call returns
- *   without waiting.  The library holds no mutable global state, so calls
- *   are reentrant and thread-safe.
+ *   without waiting.  The library holds no mutable global state apart from
+ *   star_decode_step_noalloc's per-GPU scratch array (see there), so the
+ *   other calls are reentrant and thread-safe.
  * - Errors: arguments are validated on the host before anything is
  *   enqueued; a negative star_status is returned and nothing runs.  A launch
  *   failure reported by the HIP runtime returns STAR_ERR_HIP.  No C++
@@ -371,6 +372,31 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
                      int32_t P, int32_t splits, float scale, float* o_part,
                      float* lse_part, const star_tensor* o, float* lse,
                      void* stream);
+
+/*
+ * star_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without the o_part / lse_part workspaces.  The
+ * split-KV partials live in a file-scope device array of
+ * STAR_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends; its address on the current device is looked up once per
+ * device.  The call allocates nothing and frees nothing.
+ *   Arguments, semantics and errors are star_decode_step's; in addition
+ *   STAR_ERR_UNSUPPORTED when the partials, P * splits * B * Hq rows of
+ *   D + 1 floats, do not fit the array (about 8000 rows at D = 128), and
+ *   STAR_ERR_HIP when the array's address cannot be obtained.
+ *   Every call on one GPU uses that GPU's one array, and each call
+ *   overwrites every partial it reads before reading it: calls that may
+ *   overlap on one GPU (different streams, different threads) race and must
+ *   not be issued.
+ */
+#define STAR_NOALLOC_SCRATCH_BYTES (4 << 20)
+int star_decode_step_noalloc(const star_tensor* q_new, const star_tensor* k_new,
+                             const star_tensor* v_new, const star_tensor* k_cache,
+                             const star_tensor* v_cache, int64_t slot, int64_t pos,
+                             double base, int32_t rope, const int64_t* part_offsets,
+                             int32_t P, int32_t splits, float scale,
+                             const star_tensor* o, float* lse, void* stream);
 
 /*
  * The attention layer around Phase 1 (the Llama-3 attention block of the

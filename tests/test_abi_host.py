@@ -333,3 +333,36 @@ def test_rope_freqs_are_the_nearest_float64(lib):
     assert lib.star_rope_freqs(8, 5e5, out) == -5
     assert lib.star_rope_freqs(128, 1.0, out) == -2
     assert lib.star_rope_freqs(128, float("inf"), out) == -2
+
+
+def test_decode_step_noalloc_validation(lib):
+    """The no-allocation decode step checks its arguments exactly as
+    star_decode_step does, then refuses partials beyond its scratch array,
+    all before it touches the GPU."""
+    qn = T(B=1, H=8, S=1, D=128)
+    kn, vn = T(B=1, H=2, S=1, D=128), T(B=1, H=2, S=1, D=128)
+    kc, vc = T(B=1, H=2, S=100, D=128), T(B=1, H=2, S=100, D=128)
+    o = T(B=1, H=8, S=1, D=128, dtype=1)
+
+    def na(q=qn, oo=o, slot=50, pos=50, offs=(0, 40, 51), splits=2, cache=(kc, vc)):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        return lib.star_decode_step_noalloc(ctypes.byref(q), ctypes.byref(kn), ctypes.byref(vn),
+                                            ctypes.byref(cache[0]), ctypes.byref(cache[1]),
+                                            slot, pos, 5e5, 1, arr, len(offs) - 1, splits, 0.1,
+                                            ctypes.byref(oo), None, None)
+    assert na(slot=49) == -2
+    assert na(q=T(B=1, H=8, S=2, D=128)) == -2
+    assert na(oo=T(B=1, H=8, S=2, D=128)) == -2
+    assert na(q=T(B=1, H=8, S=1, D=128, dtype=1)) == -3
+    assert na(offs=(0, 60, 51)) == -2
+    assert na(splits=0) == -2
+    # 128 partitions x 8 chunks x 64 heads x 129 floats: far past the 4 MiB array
+    big = (T(B=1, H=8, S=9000, D=128), T(B=1, H=8, S=9000, D=128))
+    q64, o64 = T(B=1, H=64, S=1, D=128), T(B=1, H=64, S=1, D=128, dtype=1)
+    kn8 = T(B=1, H=8, S=1, D=128)
+    arr = (ctypes.c_int64 * 129)(*(list(range(0, 8192, 64)) + [8193]))
+    assert lib.star_decode_step_noalloc(ctypes.byref(q64), ctypes.byref(kn8), ctypes.byref(kn8),
+                                        ctypes.byref(big[0]), ctypes.byref(big[1]), 8192, 8192,
+                                        5e5, 1, arr, 128, 8, 0.1, ctypes.byref(o64), None,
+                                        None) == -5
+    assert _lib.STAR_NOALLOC_SCRATCH_BYTES == 4 << 20
