@@ -37,6 +37,11 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "phase1_flash_llama8b-128k_pmc.txt"
 FLASH_SRC = os.path.join(ROOT, "block_sparse_amd", "csrc", "flash2.hip")
 
 
+def progress(msg: str):
+    """One line per finished stage, on stderr (the JSON line owns stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def phase1_pairs(L: int, b: int, a: int) -> int:
     """Useful (query, key) pairs of Phase 1 per head: block 1 is causal over
     itself; block i >= 2 sees a anchor keys plus its causal prefix."""
@@ -219,37 +224,228 @@ def phase1_layer(w, ev, reps=3):
 
 
 def decode_cold(st, dev, w, ev, samples=16):
-    """Decode steps timed one at a time, each after a 1 GiB device read that
-    evicts the L2 caches and the 256 MiB Infinity Cache, so every K/V byte
-    comes from HBM.  The flush reads rather than writes: a written flush
-    leaves dirty lines whose write-back then competes with the timed reads
-    (it halves a plain streaming read's rate on this chip).  Re-runs decode
-    steps spread over 0..T-1 after the timed pass (the cache rows they
-    append hold the same values)."""
+    """Decode steps with cold caches: each step runs right after a 1 GiB
+    device read that evicts the L2 caches and the 256 MiB Infinity Cache, so
+    every K/V byte comes from HBM.  The flush reads rather than writes: a
+    written flush leaves dirty lines whose write-back then competes with the
+    timed reads (it halves a plain streaming read's rate on this chip).
+
+    An event recorded between the flush and the step would itself cost
+    several microseconds (the command processor finishes the flush and the
+    marker before it dispatches the step), so the step is timed as the
+    difference of two interleaved sequences: [event, flush, step, event] and
+    [event, flush, event].  Re-runs decode steps spread over 0..T-1 after
+    the timed pass (the cache rows they append hold the same values)."""
     import numpy as np
     import torch
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     ts = sorted(set(np.linspace(0, w.T - 1, min(samples, w.T)).astype(int).tolist()))
-    recs = []
-    for i, t in enumerate(ts):
+    # untimed round first: the first reduction loads its kernel
+    for _ in range(2):
         torch.sum(flush, dim=0, out=sink)
-        e0, e1 = ev(), ev()
+        st.decode(ts[0], dev["qd"][:, :, ts[0]:ts[0] + 1], dev["kd"][:, :, ts[0]:ts[0] + 1],
+                  dev["vd"][:, :, ts[0]:ts[0] + 1])
+    torch.cuda.synchronize()
+    with_step, flush_only = [], []
+    for t in ts:
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
+        torch.sum(flush, dim=0, out=sink)
         st.decode(t, dev["qd"][:, :, t:t + 1], dev["kd"][:, :, t:t + 1],
                   dev["vd"][:, :, t:t + 1])
         e1.record()
-        recs.append((t, e0, e1))
+        e2.record()
+        torch.sum(flush, dim=0, out=sink)
+        e3.record()
+        with_step.append((t, e0, e1))
+        flush_only.append((e2, e3))
     torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for _, e0, e1 in recs]
-    byts = [decode_bytes(w, t) for t, _, _ in recs]
-    us = float(np.mean(ms)) * 1e3
-    gbps = float(np.sum(byts) / (np.sum(ms) * 1e-3) / 1e9)
+    a = [e0.elapsed_time(e1) for _, e0, e1 in with_step]
+    f = [e2.elapsed_time(e3) for e2, e3 in flush_only]
+    step_ms = float(np.median(a) - np.median(f))
+    byts = float(np.mean([decode_bytes(w, t) for t, _, _ in with_step]))
+    gbps = byts / (step_ms * 1e-3) / 1e9
     del flush
-    return {"us_per_step": us, "gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBS,
-            "steps_sampled": len(ts),
-            "note": "each step after a 1 GiB read that flushes L2 and Infinity Cache"}
+    return {"us_per_step": step_ms * 1e3, "gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBS,
+            "steps_sampled": len(ts), "flush_us": float(np.median(f)) * 1e3,
+            "flush_us_std": float(np.std(f)) * 1e3,
+            "note": "each step right after a 1 GiB read that flushes L2 and Infinity Cache; "
+                    "median of [flush + step] minus median of [flush] over interleaved "
+                    "samples"}
+
+
+def query_flops(w) -> float:
+    """Algorithmic FLOPs of the Phase-2 query partials: query row r (at
+    position L + r) sees L + r + 1 keys, 4 D FLOPs per (row, key) pair."""
+    return 4.0 * w.D * w.Hq * w.B * sum(w.L + r + 1 for r in range(w.Lq))
+
+
+def query_bytes(w) -> int:
+    """K and V bytes the query partials read: every key once per KV head."""
+    return (w.L + w.Lq) * w.Hkv * w.B * w.D * 2 * 2
+
+
+def phase2_query(st, w, ev, reps=20):
+    """The Phase-2 query partials alone (the flash kernel in partial mode),
+    back to back, against min(MFMA peak, arithmetic intensity x HBM peak)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_amd import phase2_partial
+    from block_sparse_amd.pipeline import partition_offsets
+    offs = partition_offsets(w.L, w.b, w.L + w.Lq)
+
+    def run():
+        phase2_partial(st.qq_r[:, :, :w.Lq], st.kc, st.vc, offs, st.sq, q_pos0=w.L,
+                       scale=st.scale, o_part=st.op_q, lse_part=st.lp_q)
+    run()
+    torch.cuda.synchronize()
+    samples = []
+    for _ in range(3):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) / reps)
+    ms = float(np.median(samples))
+    fl, by = query_flops(w), query_bytes(w)
+    tflops = fl / (ms * 1e-3) / 1e12
+    gbps = by / (ms * 1e-3) / 1e9
+    ai = fl / by
+    roof = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+    return {"us": ms * 1e3, "tflops": tflops, "gbps": gbps, "flops": fl, "bytes": by,
+            "arith_intensity": ai, "roofline_tflops": roof, "frac_of_roofline": tflops / roof,
+            "splits": st.sq,
+            "note": "star_phase2_partial for the query rows alone; roofline = "
+                    "min(bf16 MFMA peak, flop/byte x HBM peak)"}
+
+
+def config_record(name, ev, rows_per_block=8, decode_steps=16):
+    """One record per workload: Phase-1 time and rate, the Phase-2 query
+    and warm decode-step times, and the parity errors of a small sampled
+    check against the oracle.  The device inputs are seeded normal draws;
+    batch 0's KV head 0 and its query heads are the seeded workload draws
+    (workloads.draw_tensor), so the oracle regenerates exactly those slices
+    and checks: block edges plus ``rows_per_block`` seeded rows of every
+    block of Phase 1, every query row, and the timed decode steps."""
+    import numpy as np
+    import torch
+
+    import oracle.star_oracle as so
+    from block_sparse_amd.pipeline import StarAttentionStep
+    from workloads import (T_K, T_KD, T_KQ, T_Q, T_QD, T_QQ, T_V, T_VD, T_VQ, WORKLOADS,
+                           bf16_bits_to_f32, draw_tensor)
+    w = WORKLOADS[name]
+    g = w.g
+    n_dec = min(w.T, decode_steps)
+    gen = torch.Generator(device="cuda").manual_seed(1000 + w.seed)
+    host = {}
+
+    def make(key, tid, H, S):
+        t = torch.empty((w.B, H, S, w.D), dtype=torch.bfloat16, device="cuda")
+        for bb in range(w.B):
+            for h in range(H):
+                t[bb, h].copy_(torch.randn((S, w.D), generator=gen, device="cuda") * w.scale)
+        nh = g if H == w.Hq else 1          # batch 0: KV head 0 and its query heads
+        bits = draw_tensor(w.seed, tid, 1, nh, S, w.D, w.scale)
+        host[key] = bf16_bits_to_f32(bits[0]).astype(np.float64)
+        t[0, :nh].copy_(torch.from_numpy(bits[0].view(np.int16)).view(torch.bfloat16))
+        return t
+
+    q, k, v = make("q", T_Q, w.Hq, w.L), make("k", T_K, w.Hkv, w.L), make("v", T_V, w.Hkv, w.L)
+    qq, kq, vq = (make("qq", T_QQ, w.Hq, w.Lq), make("kq", T_KQ, w.Hkv, w.Lq),
+                  make("vq", T_VQ, w.Hkv, w.Lq))
+    qd, kd, vd = (make("qd", T_QD, w.Hq, n_dec), make("kd", T_KD, w.Hkv, n_dec),
+                  make("vd", T_VD, w.Hkv, n_dec))
+    st = StarAttentionStep(w.B, w.Hq, w.Hkv, w.D, w.L, w.b, w.Lq, n_dec, rope=w.rope,
+                           base=w.base)
+    st.load_context(v)
+    st.rope_context(q, k)
+    st.phase1()
+    torch.cuda.synchronize()
+    e = [(ev(), ev()) for _ in range(2)]
+    for e0, e1 in e:
+        e0.record()
+        st.phase1()
+        e1.record()
+    torch.cuda.synchronize()
+    p1_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in e]))
+    fl = phase1_flops(w)
+    rec = {"workload": name, "phase1_ms": p1_ms,
+           "phase1_tflops": fl / (p1_ms * 1e-3) / 1e12,
+           "phase1_frac_of_peak": fl / (p1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "context_tokens_per_s": w.B * w.L / (p1_ms * 1e-3)}
+    st.query(qq, kq, vq)
+    if n_dec:
+        e0, e1 = ev(), ev()
+        e0.record()
+        for t in range(n_dec):
+            st.decode(t, qd[:, :, t:t + 1], kd[:, :, t:t + 1], vd[:, :, t:t + 1])
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / n_dec
+        byts = sum(decode_bytes(w, t) for t in range(n_dec)) / n_dec
+        rec.update({"decode_us_per_step": dms * 1e3, "decode_gbps": byts / (dms * 1e-3) / 1e9,
+                    "decode_frac_of_hbm_peak": byts / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    "decode_steps_timed": n_dec})
+    torch.cuda.synchronize()
+    # parity on the seeded slices
+    scale = 1.0 / math.sqrt(w.D)
+    rng = np.random.default_rng(w.seed)
+    pos = []
+    for s0, e0_ in so.blocks(w.L, w.b):
+        pos += [s0, s0 + 1, e0_ - 2, e0_ - 1]
+        pos += (s0 + rng.choice(e0_ - s0, min(rows_per_block, e0_ - s0), replace=False)).tolist()
+    pos = np.unique(np.clip(np.array(pos), 0, w.L - 1))
+    rot = (lambda x, p: so.round_bf16(so.rope(x, p, w.base))) if w.rope else (lambda x, p: x)
+    K = rot(host["k"][0], np.arange(w.L))
+    V = host["v"][0]
+    pq = w.L + np.arange(w.Lq)
+    pd = w.L + w.Lq + np.arange(n_dec)
+    Kc = np.concatenate([K, rot(host["kq"][0], pq), rot(host["kd"][0], pd)])
+    Vc = np.concatenate([V, host["vq"][0], host["vd"][0]])
+    parts = so.partitions(w.L, w.b, w.L + w.Lq + n_dec)
+    Vw = np.concatenate([V, np.abs(V)], axis=-1)
+    pos_t = torch.from_numpy(pos).cuda()
+    err = {"phase1_max_abs": 0.0, "phase1_mean_abs": 0.0, "phase1_lse": 0.0,
+           "query_max_abs": 0.0, "query_lse": 0.0, "decode_max_abs": 0.0, "decode_lse": 0.0}
+    ok = True
+    for h in range(g):
+        rw, rl = so.phase1_rows(rot(host["q"][h][pos], pos), pos, K, Vw, w.b, w.a, scale)
+        ro, wabs = rw[:, :w.D], rw[:, w.D:]
+        go = st.o1[0, h].index_select(0, pos_t).float().cpu().numpy().astype(np.float64)
+        gl = st.lse1[0, h].index_select(0, pos_t).cpu().numpy().astype(np.float64)
+        d = np.abs(go - ro)
+        ok &= bool((d <= np.maximum(1e-2, 2.0 ** -8 * np.abs(ro) + 2.0 ** -9 * wabs + 1e-4)).all())
+        err["phase1_max_abs"] = max(err["phase1_max_abs"], float(d.max()))
+        err["phase1_mean_abs"] = max(err["phase1_mean_abs"], float(d.mean()))
+        err["phase1_lse"] = max(err["phase1_lse"], float(np.abs(gl - rl).max()))
+        rows = np.concatenate([rot(host["qq"][h], pq), rot(host["qd"][h], pd)])
+        o, l, _, _ = so.phase2(rows, np.concatenate([pq, pd]), Kc, Vc, parts, scale)
+        if w.Lq:
+            err["query_max_abs"] = max(err["query_max_abs"], float(np.abs(
+                st.o2[0, h].cpu().numpy() - o[:w.Lq]).max()))
+            err["query_lse"] = max(err["query_lse"], float(np.abs(
+                st.lse2[0, h].cpu().numpy() - l[:w.Lq]).max()))
+        if n_dec:
+            err["decode_max_abs"] = max(err["decode_max_abs"], float(np.abs(
+                st.od[0, h, :n_dec].cpu().numpy() - o[w.Lq:]).max()))
+            err["decode_lse"] = max(err["decode_lse"], float(np.abs(
+                st.lsed[:n_dec, 0, h].cpu().numpy() - l[w.Lq:]).max()))
+    ok &= (err["phase1_mean_abs"] <= 1e-3 and err["phase1_lse"] <= 1e-3
+           and err["query_max_abs"] <= 1e-2 and err["query_lse"] <= 1e-3
+           and err["decode_max_abs"] <= 1e-2 and err["decode_lse"] <= 1e-3)
+    rec["parity"] = {**err, "within_tolerance": bool(ok), "heads_checked": g,
+                     "phase1_rows_per_head": int(pos.size), "query_rows": w.Lq,
+                     "decode_steps": n_dec,
+                     "checked": "batch 0, KV head 0 and its query heads, vs the fp64 oracle"}
+    del st, q, k, v, qq, kq, vq, qd, kd, vd
+    torch.cuda.empty_cache()
+    return rec
 
 
 def hbm_stream(ev, mib=1024, reps=5):
@@ -283,6 +479,62 @@ def hbm_stream(ev, mib=1024, reps=5):
             "note": "star_stream_read over 1 GiB (a plain streaming read, 16-byte nontemporal loads)"}
 
 
+def cpu_full_oracle():
+    """The whole oracle (Phase 1 over every row and head, the query rows and
+    every decode step) on the two workloads small enough for it: tiny and
+    llama8b-16k.  (At 8B-128K the oracle's explicit score matrices hold
+    ~7e13 fp64 products, about ten minutes of host time, so the default
+    cpu_baseline times a bounded sample instead.)"""
+    import numpy as np
+
+    import oracle.star_oracle as so
+    from workloads import WORKLOADS, as_f64, inputs
+    out = {}
+    for name in ("tiny", "llama8b-16k"):
+        w = WORKLOADS[name]
+        x = {n: as_f64(t) for n, t in inputs(w, as_bf16=True).items()}
+        t0 = time.perf_counter()
+        so.star_attention(w, x)
+        dt = time.perf_counter() - t0
+        out[name] = {"seconds": dt, "context_tokens_per_s": w.B * w.L / dt,
+                     "note": "fp64 numpy oracle, whole workload incl. RoPE, Phase 1, query "
+                             "and every decode step"}
+    return out
+
+
+def trace_summary(root: str) -> str:
+    """Per-kernel count, mean, median and min duration (us) from the
+    kernel_trace.csv files a ``rocprofv3 --kernel-trace --output-format csv``
+    run wrote under ``root``, one line per (kernel, workgroup count)."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return f"no *kernel_trace.csv under {root}"
+    agg = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "?")
+                try:
+                    grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)))
+                    wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 1)))
+                    d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                except (KeyError, ValueError):
+                    continue
+                short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))
+                short = re.sub(r"^void ", "", short)
+                agg.setdefault((short[:60], grid // max(wg, 1)), []).append(d)
+    tot = sum(sum(v) for v in agg.values())
+    lines = [f"{'kernel':60s} {'workgroups':>10s} {'calls':>6s} {'mean_us':>10s} "
+             f"{'median_us':>10s} {'min_us':>10s} {'share':>6s}"]
+    for (n, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{n:60s} {wg:10d} {len(v):6d} {statistics.mean(v):10.2f} "
+                     f"{statistics.median(v):10.2f} {min(v):10.2f} {100 * sum(v) / tot:5.1f}%")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,7 +557,20 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first "
                          "(reference kernel for rocprofv3 byte counters)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload records (timing + sampled parity)")
+    ap.add_argument("--configs", default=None,
+                    help="comma-separated workloads for the per-workload records "
+                         "(default: all five)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the whole oracle on the tiny and llama8b-16k workloads")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="print the per-kernel summary of a rocprofv3 --output-format csv "
+                         "kernel trace found under DIR, then exit (no GPU)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "
               "run it with --gpus 1", file=sys.stderr)
@@ -354,9 +619,11 @@ def main():
         if rec is not None:
             rec["dec"][1].record()
 
+    progress(f"{w.name}: inputs resident")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    progress("warm-up done")
     recs = [{"p1": [ev(), ev(), ev()], "dec": [ev(), ev()]} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -365,9 +632,11 @@ def main():
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
     ms_step = total * 1e3 / args.steps
+    progress(f"timed steps done: {ms_step:.2f} ms per step")
 
     rope_ms = np.mean([r["p1"][0].elapsed_time(r["p1"][1]) for r in recs])
-    p1_ms = np.mean([r["p1"][1].elapsed_time(r["p1"][2]) for r in recs])
+    p1_samples = [r["p1"][1].elapsed_time(r["p1"][2]) for r in recs]
+    p1_ms = np.mean(p1_samples)
     flops = phase1_flops(w)
     p1_tflops = flops / (p1_ms * 1e-3) / 1e12
     out = {
@@ -382,7 +651,8 @@ def main():
                    "query_tokens": w.Lq, "decode_steps": w.T, "rope_base": w.base,
                    "splits_query": st.sq, "splits_decode": st.sd,
                    "phase1_only": bool(args.phase1_only)},
-        "phase1": {"kernel_ms": p1_ms, "rope_ms": rope_ms,
+        "phase1": {"kernel_ms": p1_ms, "kernel_median_ms": float(np.median(p1_samples)),
+                   "kernel_min_ms": float(np.min(p1_samples)), "rope_ms": rope_ms,
                    "context_tokens_per_s": w.B * w.L / (p1_ms * 1e-3),
                    "context_tokens_per_s_with_rope": w.B * w.L / ((p1_ms + rope_ms) * 1e-3),
                    "tflops": p1_tflops, "algorithmic_flops": flops},
@@ -399,16 +669,32 @@ def main():
                          "frac_of_hbm_peak": byts / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "note": "whole decode step (RoPE, KV append, partials, merge), "
                                  "K+V bytes of every visible token"}
+    if not args.phase1_only and w.Lq > 0:
+        out["phase2_query"] = phase2_query(st, w, ev)
     if not args.phase1_only and w.T > 0 and not args.no_cold:
         out["decode_cold"] = decode_cold(st, dev, w, ev)
+        progress("cold decode done")
     if not args.phase1_only and w.T > 0:
         out["hbm_stream"] = hbm_stream(ev)
     if w.rope and not args.no_variants:
         out["phase1_variants"] = phase1_variants(st, dev, w, x, ev)
+        progress("Phase-1 variants done")
     if not args.no_layer:
         out["phase1_layer"] = phase1_layer(w, ev)
+        progress("attention layer done")
+    del st, dev
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        names = args.configs.split(",") if args.configs else list(WORKLOADS)
+        out["per_config"] = []
+        for n in names:
+            out["per_config"].append(config_record(n, ev))
+            progress(f"per-workload record {n} done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
+        progress("cpu baseline done")
+        if args.cpu_full:
+            out["cpu_full_oracle"] = cpu_full_oracle()
     print(json.dumps(out), flush=True)
 
 

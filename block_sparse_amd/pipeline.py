@@ -80,7 +80,9 @@ class StarAttentionStep:
         self.lsed = torch.empty((max(T, 1), B, Hq), dtype=torch.float32, device=dev)
         self.P = -(-L // b)
         part_len = min(b, L)
-        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 512, 512)
+        # query chunks: one workgroup per CU (256 at 8B-128K) -- measured
+        # 164 us against 190 us for two rounds of half-length chunks
+        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 256, 512)
         self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 256, 512)
         nq = self.P * self.sq
         nd = self.P * self.sd

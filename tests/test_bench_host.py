@@ -62,3 +62,32 @@ def test_traffic_only_for_the_profiled_kernel(tmp_path, monkeypatch):
     other.write_text("// another kernel\n")
     monkeypatch.setattr(bench, "FLASH_SRC", str(other))
     assert bench.pmc_traffic() is None
+
+
+def test_query_work_figures():
+    """Query row r at position L + r sees every key up to itself (L + r + 1
+    keys); K and V are each read once per KV head."""
+    bench = load_bench()
+    from workloads import WORKLOADS
+    w = WORKLOADS["llama8b-128k"]
+    pairs = sum(len(range(0, w.L + r + 1)) for r in range(w.Lq))
+    assert bench.query_flops(w) == 4.0 * w.D * w.Hq * w.B * pairs
+    assert bench.query_flops(w) == pytest.approx(1.3747e11, rel=1e-3)
+    assert bench.query_bytes(w) == (w.L + w.Lq) * w.Hkv * w.D * 4
+
+
+def test_trace_summary_reads_rocprof_csv(tmp_path):
+    """The per-kernel summary of a rocprofv3 csv kernel trace: count, mean,
+    median and min per (kernel, workgroup count)."""
+    bench = load_bench()
+    hdr = ("Kind,Agent_Id,Queue_Id,Stream_Id,Thread_Id,Dispatch_Id,Kernel_Id,Kernel_Name,"
+           "Correlation_Id,Start_Timestamp,End_Timestamp,Private_Segment_Size,"
+           "Group_Segment_Size,Workgroup_Size_X,Workgroup_Size_Y,Workgroup_Size_Z,"
+           "Grid_Size_X,Grid_Size_Y,Grid_Size_Z\n")
+    rows = []
+    for i, d in enumerate((10_000, 30_000, 20_000)):
+        rows.append(f'KERNEL_DISPATCH,1,1,1,1,{i},1,"star::(anonymous namespace)::k(star::P)",'
+                    f'{i},{1000 * i},{1000 * i + d},0,0,512,1,1,{512 * 256},1,1\n')
+    (tmp_path / "run_kernel_trace.csv").write_text(hdr + "".join(rows))
+    out = bench.trace_summary(str(tmp_path)).splitlines()
+    assert out[1].split()[:6] == ["star::k", "256", "3", "20.00", "20.00", "10.00"]
