@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libstarattn.so")
+# STAR_ATTN_LIB names another build of the library (the host tests load an
+# AddressSanitizer build through it)
+LIB_PATH = os.environ.get("STAR_ATTN_LIB") or os.path.join(HERE, "libstarattn.so")
 
 STAR_BF16 = 0
 STAR_F32 = 1
