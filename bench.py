@@ -502,6 +502,36 @@ def cpu_full_oracle():
     return out
 
 
+def _short_kernel_name(name: str) -> str:
+    """Kernel name without namespace noise and argument list.  rocprofv3
+    leaves some names with a __bf16 template argument mangled (``_ZN4star
+    12_GLOBAL__N_111rope_kernelIDF16bEE...``): their nested name and simple
+    template arguments are decoded here."""
+    if name.startswith("_ZN"):
+        parts, i = [], 3
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            parts.append(name[j:j + n])
+            i = j + n
+        targs = ""
+        if name[i:i + 1] == "I" and "E" in name[i:]:
+            code = name[i + 1:name.index("E", i)]
+            targs = "<" + {"DF16b": "__bf16", "f": "float", "d": "double"}.get(code, code) + ">"
+        return "::".join(x for x in parts if not x.startswith("_GLOBAL__N")) + targs
+    short = name.replace("(anonymous namespace)::", "")
+    if short.endswith(")"):                       # drop the argument list
+        depth = 0
+        for i in range(len(short) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(short[i], 0)
+            if depth == 0:
+                short = short[:i]
+                break
+    return re.sub(r"^void ", "", short)
+
+
 def trace_summary(root: str) -> str:
     """Per-kernel count, mean, median and min duration (us) from the
     kernel_trace.csv files a ``rocprofv3 --kernel-trace --output-format csv``
@@ -523,8 +553,7 @@ def trace_summary(root: str) -> str:
                     d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 except (KeyError, ValueError):
                     continue
-                short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))
-                short = re.sub(r"^void ", "", short)
+                short = _short_kernel_name(name)
                 agg.setdefault((short[:60], grid // max(wg, 1)), []).append(d)
     tot = sum(sum(v) for v in agg.values())
     lines = [f"{'kernel':60s} {'workgroups':>10s} {'calls':>6s} {'mean_us':>10s} "

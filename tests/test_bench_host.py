@@ -91,3 +91,18 @@ def test_trace_summary_reads_rocprof_csv(tmp_path):
     (tmp_path / "run_kernel_trace.csv").write_text(hdr + "".join(rows))
     out = bench.trace_summary(str(tmp_path)).splitlines()
     assert out[1].split()[:6] == ["star::k", "256", "3", "20.00", "20.00", "10.00"]
+
+
+def test_short_kernel_names():
+    """Namespace noise and argument lists go; names rocprofv3 leaves mangled
+    (a __bf16 template argument) are decoded."""
+    bench = load_bench()
+    f = bench._short_kernel_name
+    assert f("_ZN4star12_GLOBAL__N_111rope_kernelIDF16bEEvNS_10RopeParamsEi") == \
+        "star::rope_kernel<__bf16>"
+    assert f("_ZN4star12_GLOBAL__N_111rope_kernelIfEEvNS_10RopeParamsEi") == \
+        "star::rope_kernel<float>"
+    assert f("star::(anonymous namespace)::stream_read_kernel(unsigned int __vector(4) const*, "
+             "long, unsigned int*)") == "star::stream_read_kernel"
+    assert f("void star::(anonymous namespace)::merge_kernel<128>(star::MergeParams)") == \
+        "star::merge_kernel<128>"
