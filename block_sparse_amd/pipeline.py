@@ -190,7 +190,10 @@ class StarAttentionStep:
                       self.ast, self.aln, self.b, self.scale, out=self.o1, lse=self.lse1,
                       sched=self.sched)
 
-    def query(self, qq, kq, vq):
+    def query(self, qq, kq, vq, events=None):
+        """The query tokens (inputs [B, H, Lq, D]).  ``events``: an optional
+        pair of timing events recorded on the stream right before and after
+        the partials call."""
         L, Lq = self.L, self.Lq
         if Lq == 0:
             return
@@ -200,9 +203,13 @@ class StarAttentionStep:
             self.qq_r[:, :, :Lq].copy_(qq)
         kv_append(kq, vq, self.kc, self.vc, slot0=L, pos0=L, base=self.base, rope=self.rope)
         offs = partition_offsets(L, self.b, L + Lq)
+        if events is not None:
+            events[0].record()
         op, lp = phase2_partial(self.qq_r[:, :, :Lq], self.kc, self.vc, offs, self.sq,
                                 q_pos0=L, scale=self.scale,
                                 o_part=self.op_q, lse_part=self.lp_q)
+        if events is not None:
+            events[1].record()
         lse_merge(op, lp, out=self.o2, lse=self.lse2)
 
     def decode(self, t, qd, kd, vd):
