@@ -334,6 +334,68 @@ def phase2_query(st, w, ev, in_step_ms, reps=20):
                     f"{reps} back to back; roofline = min(bf16 MFMA peak, flop/byte x HBM peak)"}
 
 
+def decode_graph(st, w, ev, n):
+    """Decode steps replayed from captured HIP graphs (star_decode_step_devpos
+    and its merge: the token's position lives in device memory and each
+    step advances it), against the eager steps whose host-side launch work
+    can exceed a short step's GPU time.
+      one_step: a graph of one step, replayed ``n`` times back to back;
+        each replay also pays the runtime's gap between graph launches.
+      sequence: ``n`` consecutive steps captured in one graph and replayed
+        once, as a per-token graph of a model with ``n`` attention layers
+        would hold them: the launch gap is paid once.
+    Writes cache rows L + Lq .. L + Lq + n - 1, as the timed steps do."""
+    import numpy as np
+    import torch
+
+    from block_sparse_amd import decode_step_devpos
+    from block_sparse_amd.pipeline import partition_offsets
+    p0 = w.L + w.Lq
+    offs = partition_offsets(w.L, w.b, st.S)       # positions up to the cache's end
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    mk = lambda H: torch.randn((w.B, H, 1, w.D), device="cuda", generator=gen).to(torch.bfloat16)
+    qb, kb, vb = mk(w.Hq), mk(w.Hkv), mk(w.Hkv)
+    ob = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device="cuda")
+    lb = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    pos = torch.full((1,), p0, dtype=torch.int64, device="cuda")
+
+    def one():
+        decode_step_devpos(qb, kb, vb, st.kc, st.vc, pos, offs, st.sd, st.op_d, st.lp_d, ob, lb,
+                           base=w.base, rope=w.rope, scale=st.scale)
+
+    torch.cuda.synchronize()
+    g1, gn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        one()
+    with torch.cuda.graph(gn):
+        for _ in range(n):
+            one()
+    out = {}
+    for name, graph, replays in (("one_step", g1, n), ("sequence", gn, 1)):
+        graph.replay()                              # untimed first replay
+        pos.fill_(p0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if int(pos.item()) != p0 + n:
+            raise RuntimeError("device position did not advance once per step")
+        out[name] = e0.elapsed_time(e1) / n
+    del g1, gn
+    byts = float(np.mean([decode_bytes(w, t) for t in range(n)]))
+    ms = out["sequence"]
+    return {"us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "one_step_graph_us_per_step": out["one_step"] * 1e3, "steps": n,
+            "note": f"{n} decode steps (star_decode_step_devpos + merge) captured in one HIP "
+                    "graph and replayed; one_step_graph: a one-step graph replayed "
+                    f"{n} times (each replay adds the runtime's gap between graph launches)"}
+
+
 def config_record(name, ev, rows_per_block=8, decode_steps=16):
     """One record per workload: Phase-1 time and rate, the Phase-2 query
     and warm decode-step times, and the parity errors of a small sampled
@@ -453,6 +515,12 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
                      "phase1_rows_per_head": int(pos.size), "query_rows": w.Lq,
                      "decode_steps": n_dec,
                      "checked": "batch 0, KV head 0 and its query heads, vs the fp64 oracle"}
+    if n_dec:
+        # after the parity check: the replays overwrite the decode rows
+        gr = decode_graph(st, w, ev, n_dec)
+        rec.update({"decode_graph_us_per_step": gr["us_per_step"],
+                    "decode_graph_frac_of_hbm_peak": gr["frac_of_hbm_peak"],
+                    "decode_one_step_graph_us_per_step": gr["one_step_graph_us_per_step"]})
     del st, q, k, v, qq, kq, vq, qd, kd, vd
     torch.cuda.empty_cache()
     return rec
@@ -715,6 +783,9 @@ def main():
     if not args.phase1_only and w.T > 0 and not args.no_cold:
         out["decode_cold"] = decode_cold(st, dev, w, ev)
         progress("cold decode done")
+    if not args.phase1_only and w.T > 0:
+        out["decode_graph"] = decode_graph(st, w, ev, w.T)
+        progress("graph decode done")
     if not args.phase1_only and w.T > 0:
         out["hbm_stream"] = hbm_stream(ev)
     if w.rope and not args.no_variants:

@@ -24,7 +24,7 @@ from ._lib import STAR_MAX_PARTS, STAR_SPLIT_ALIGN, StarError  # noqa: F401
 __all__ = ["rope_apply", "rope_freqs", "kv_append", "decode_prepare", "phase1_blocklocal", "phase1_rope",
            "phase1_prefix", "sched_workspace", "SCHED_INTS",
            "gather_rows", "pulsar_prefix", "phase2_partial", "lse_merge", "decode_step",
-           "decode_step_noalloc",
+           "decode_step_devpos", "decode_step_noalloc",
            "Context", "rmsnorm", "linear", "split_ranges", "stream_read",
            "StarError", "library"]
 
@@ -361,6 +361,39 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, slot: int, pos: int, part
                                     float(scale), _ptr(o_part), _ptr(lse_part),
                                     ctypes.byref(do), _ptr(lse), _stream(q_new))
     _lib.check("star_decode_step", st)
+    return out, lse
+
+
+def decode_step_devpos(q_new, k_new, v_new, k_cache, v_cache, pos_dev, part_offsets,
+                       splits: int, o_part, lse_part, out, lse=None, base: float = 500000.0,
+                       rope: bool = True, scale: float | None = None):
+    """:func:`decode_step` with the token's position in device memory
+    (``pos_dev``: a one-element int64 device tensor, read at the start of
+    the step and advanced by one at its end), so that a captured graph of
+    the call serves every step.  ``part_offsets[-1]`` bounds the positions
+    the call may run at (star_decode_step_devpos)."""
+    B, Hq, _, D = q_new.shape
+    P = len(part_offsets) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if (pos_dev.dtype != torch.int64 or pos_dev.numel() != 1 or pos_dev.device.type != "cuda"):
+        raise ValueError("pos_dev must be a one-element int64 device tensor")
+    N = P * splits
+    for t, n in ((o_part, N * B * Hq * D), (lse_part, N * B * Hq)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+            raise ValueError("o_part / lse_part must be contiguous fp32 buffers of the full size")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != B * Hq):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq] tensor")
+    offs = (ctypes.c_int64 * (P + 1))(*[int(x) for x in part_offsets])
+    d = [_desc(t) for t in (q_new, k_new, v_new, k_cache, v_cache)]
+    do = _desc(out)
+    st = library().star_decode_step_devpos(*[ctypes.byref(x) for x in d], _ptr(pos_dev),
+                                           float(base), int(bool(rope)), offs, int(P),
+                                           int(splits), float(scale), _ptr(o_part),
+                                           _ptr(lse_part), ctypes.byref(do), _ptr(lse),
+                                           _stream(q_new))
+    _lib.check("star_decode_step_devpos", st)
     return out, lse
 
 

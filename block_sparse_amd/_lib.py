@@ -30,7 +30,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("star_rope_apply", "star_rope_freqs", "star_kv_append", "star_decode_prepare", "star_phase1_blocklocal",
            "star_phase1_prefix", "star_phase1_rope", "star_gather_rows", "star_stream_read", "star_pulsar_prefix",
            "star_phase2_partial", "star_lse_merge", "star_decode_step",
-           "star_decode_step_noalloc",
+           "star_decode_step_devpos", "star_decode_step_noalloc",
            "star_context_create", "star_context_destroy", "star_rmsnorm", "star_linear",
            "star_status_string",
            "star_abi_version")
@@ -71,6 +71,8 @@ _SIGS = {
     "star_lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _i64, _T, _vp, _vp]),
     "star_decode_step": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32, _P(_i64), _i32,
                                         _i32, _f32, _vp, _vp, _T, _vp, _vp]),
+    "star_decode_step_devpos": (ctypes.c_int, [_T, _T, _T, _T, _T, _vp, _f64, _i32, _P(_i64),
+                                               _i32, _i32, _f32, _vp, _vp, _T, _vp, _vp]),
     "star_decode_step_noalloc": (ctypes.c_int, [_T, _T, _T, _T, _T, _i64, _i64, _f64, _i32,
                                                 _P(_i64), _i32, _i32, _f32, _T, _vp, _vp]),
     "star_context_create": (ctypes.c_int, [_P(_vp)]),

@@ -472,7 +472,7 @@ int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
                      const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
                      int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
                      float scale, float* o_part, float* lse_part, const star_tensor* o,
-                     float* lse, void* stream, bool ws_given) {
+                     float* lse, void* stream, bool ws_given, int64_t* pos_dev) {
   int s;
   if ((s = check_qkv(q_new, k_cache, v_cache)) != STAR_OK) return s;
   if ((s = check_tensor(k_new, false)) != STAR_OK) return s;
@@ -486,6 +486,13 @@ int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
   if (o->B != q_new->B || o->H != q_new->H || o->S != 1 || o->D != q_new->D) return STAR_ERR_SHAPE;
   int64_t chunk[STAR_MAX_PARTS];
   if ((s = check_parts(part_offsets, P, splits, k_cache->S, chunk)) != STAR_OK) return s;
+  if (pos_dev != nullptr) {
+    // the position is read on the device; the host checks only that the
+    // last partition can hold one
+    if (reinterpret_cast<uintptr_t>(pos_dev) & 7u) return STAR_ERR_ALIGN;
+    if (part_offsets[P - 1] >= part_offsets[P]) return STAR_ERR_SHAPE;
+    slot = pos = part_offsets[P - 1];
+  }
   // position-contiguous cache: the token's row is its position
   if (slot != pos || slot < part_offsets[0] || slot >= part_offsets[P]) return STAR_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return STAR_ERR_SHAPE;
@@ -501,6 +508,8 @@ int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
   p.kn = ref(k_new);
   p.vn = ref(v_new);
   p.slot = slot;
+  p.pos_dev = pos_dev;
+  p.pos_end = part_offsets[P];
   if (p.rope) fill_inv_freq(p.inv_freq, q_new->D, base);
   if ((s = hip_status(star::launch_decode(p, (hipStream_t)stream))) != STAR_OK) return s;
   // the merge runs as the next launch on the same stream: the kernel
@@ -520,6 +529,7 @@ int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
   m.osH = o->sH;
   m.osS = o->sS;
   m.lse = lse;
+  m.pos_inc = pos_dev;
   return hip_status(star::launch_merge(m, (hipStream_t)stream));
 }
 
@@ -535,7 +545,19 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
                      float* lse, void* stream) {
   return star::decode_step_impl(q_new, k_new, v_new, k_cache, v_cache, slot, pos, base, rope,
                                 part_offsets, P, splits, scale, o_part, lse_part, o, lse, stream,
-                                true);
+                                true, nullptr);
+}
+
+int star_decode_step_devpos(const star_tensor* q_new, const star_tensor* k_new,
+                            const star_tensor* v_new, const star_tensor* k_cache,
+                            const star_tensor* v_cache, int64_t* pos, double base, int32_t rope,
+                            const int64_t* part_offsets, int32_t P, int32_t splits, float scale,
+                            float* o_part, float* lse_part, const star_tensor* o, float* lse,
+                            void* stream) {
+  if (pos == nullptr) return STAR_ERR_NULL;
+  return star::decode_step_impl(q_new, k_new, v_new, k_cache, v_cache, 0, 0, base, rope,
+                                part_offsets, P, splits, scale, o_part, lse_part, o, lse, stream,
+                                true, pos);
 }
 
 int star_rmsnorm(const star_tensor* x, const void* gamma, float eps, const star_tensor* y,

@@ -34,6 +34,7 @@ namespace star {
 namespace {
 
 constexpr int NWD = 8;      // waves per workgroup
+constexpr int64_t kSplitAlign = STAR_SPLIT_ALIGN;
 constexpr int KTD = 32;     // keys per wave tile
 constexpr float kRescaleLog2 = 8.0f;
 
@@ -94,42 +95,64 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
   const int kvh = rr % p.Hkv;
   const int b = rr / p.Hkv;
   const int part = cs / p.splits, sp = cs - part * p.splits;
-  const int64_t c0 = p.offs[part] + (int64_t)sp * p.chunk[part];
-  int64_t c1 = min(c0 + p.chunk[part], p.offs[part + 1]);
+  // the token's position and cache row: kernel arguments, or read from
+  // device memory (then the last partition ends right after the token, and
+  // a position outside [offs[P-1], pos_end) leaves every chunk empty and
+  // writes no cache row)
+  int64_t q_pos0 = p.q_pos0, slot = p.slot;
+  int64_t part_end = p.offs[part + 1], chunk = p.chunk[part];
+  bool pos_ok = true;
+  if constexpr (FUSED) {
+    if (p.pos_dev != nullptr) {
+      const uint64_t raw = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p.pos_dev),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)raw);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(raw >> 32));
+      q_pos0 = slot = (int64_t)(((uint64_t)hi << 32) | lo);
+      pos_ok = q_pos0 >= p.offs[p.P - 1] && q_pos0 < p.pos_end;
+      if (part == p.P - 1) {
+        part_end = q_pos0 + 1;
+        const int64_t n = pos_ok ? part_end - p.offs[part] : 0;
+        chunk = ((n + p.splits - 1) / p.splits + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+      }
+    }
+  }
+  const int64_t c0 = p.offs[part] + (int64_t)sp * chunk;
+  int64_t c1 = min(c0 + chunk, part_end);
   c1 = min(c1, p.kv_rows);
   // rows after the last query position are visible to no row: never read
   // them (they may be cache slots not written yet)
-  c1 = min(c1, p.q_pos0 + p.Lq);
-  if (c1 < c0) c1 = c0;
+  c1 = min(c1, q_pos0 + p.Lq);
+  if (c1 < c0 || !pos_ok) c1 = c0;
 
   const int nrows = p.g * (int)p.Lq;
   const bool row_ok = n < nrows;
   const int hh = n % p.g;
   const int qi = n / p.g;
   const int head = kvh * p.g + hh;
-  const int64_t qpos = p.q_pos0 + qi;
-  const int64_t min_qpos = p.q_pos0;   // rows are ordered by query index
+  const int64_t qpos = q_pos0 + qi;
+  const int64_t min_qpos = q_pos0;     // rows are ordered by query index
 
   if constexpr (FUSED) {
     // the workgroup whose chunk holds the new token's slot appends its K/V
     // row (K rotated like q, one pair per thread) before any of its waves
     // loads the chunk
-    if (p.slot >= c0 && p.slot < c1) {
+    if (pos_ok && slot >= c0 && slot < c1) {
       const int half = D / 2;
       const __bf16* kn = reinterpret_cast<const __bf16*>(p.kn.data) + (int64_t)b * p.kn.sB +
                          (int64_t)kvh * p.kn.sH;
       const __bf16* vn = reinterpret_cast<const __bf16*>(p.vn.data) + (int64_t)b * p.vn.sB +
                          (int64_t)kvh * p.vn.sH;
       __bf16* kc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.k.data)) +
-                   (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH + p.slot * p.k.sS;
+                   (int64_t)b * p.k.sB + (int64_t)kvh * p.k.sH + slot * p.k.sS;
       __bf16* vc = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(p.v.data)) +
-                   (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH + p.slot * p.v.sS;
+                   (int64_t)b * p.v.sB + (int64_t)kvh * p.v.sH + slot * p.v.sS;
       if (tid < half) {
         const int j = tid;
         __bf16 y1 = kn[j], y2 = kn[j + half];
         if (p.rope) {
           double c, sn, r1, r2;
-          rope_cs((double)p.q_pos0, p.inv_freq[j], c, sn);
+          rope_cs((double)q_pos0, p.inv_freq[j], c, sn);
           rope_rotate64((double)(float)kn[j], (double)(float)kn[j + half], c, sn, r1, r2);
           y1 = f64_to_bf16(r1);
           y2 = f64_to_bf16(r2);
@@ -239,7 +262,7 @@ __global__ __launch_bounds__(NWD * 64) void decode_kernel(const DecodeParams p) 
       const int idx = tid + NWD * 64 * i, r = idx / (D / 2), j = idx % (D / 2);
       if (r < 16) {
         double c, sn, y1, y2;
-        rope_cs((double)(p.q_pos0 + r / p.g), qth[i], c, sn);
+        rope_cs((double)(q_pos0 + r / p.g), qth[i], c, sn);
         rope_rotate64((double)(float)qx1[i], (double)(float)qx2[i], c, sn, y1, y2);
         q_rot[r * D + j] = f64_to_bf16(y1);
         q_rot[r * D + j + D / 2] = f64_to_bf16(y2);

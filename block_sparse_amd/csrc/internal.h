@@ -86,6 +86,13 @@ struct DecodeParams {
   TensorRef kn, vn;        // the new token's K (un-rotated) and V, [B, Hkv, 1, D]
   int64_t slot;            // cache row the new token is written to
   double inv_freq[64];     // theta_j of pair j (fused rope)
+  // device-resident position (star_decode_step_devpos): when set, the
+  // token's position (= its cache row) is read from *pos_dev at the start
+  // of the launch instead of q_pos0 / slot; the last partition then ends
+  // right after it.  Positions outside [offs[P - 1], pos_end) make the step
+  // write nothing to the cache and produce empty partials.
+  const int64_t* pos_dev;
+  int64_t pos_end;
 };
 
 bool decode_supported(int g, int64_t Lq, int D);
@@ -93,13 +100,14 @@ hipError_t launch_decode(DecodeParams& p, hipStream_t stream);
 
 // star_decode_step (abi.cpp): validation, then the fused decode launch and
 // the merge; ws_given == false validates everything but the workspaces and
-// launches nothing
+// launches nothing; pos_dev != nullptr: the position is read on the device
+// (star_decode_step_devpos) and slot / pos are ignored
 int decode_step_impl(const star_tensor* q_new, const star_tensor* k_new,
                      const star_tensor* v_new, const star_tensor* k_cache,
                      const star_tensor* v_cache, int64_t slot, int64_t pos, double base,
                      int32_t rope, const int64_t* part_offsets, int32_t P, int32_t splits,
                      float scale, float* o_part, float* lse_part, const star_tensor* o,
-                     float* lse, void* stream, bool ws_given);
+                     float* lse, void* stream, bool ws_given, int64_t* pos_dev = nullptr);
 
 struct RopeParams {
   TensorRef x;
@@ -151,6 +159,7 @@ struct MergeParams {
   int32_t o_f32;
   int64_t osB, osH, osS;
   float* lse;
+  int64_t* pos_inc;      // when set, one thread adds 1 to *pos_inc (device-position decode)
 };
 
 hipError_t launch_merge(MergeParams& p, hipStream_t stream);

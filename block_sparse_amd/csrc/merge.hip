@@ -111,6 +111,9 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
     for (int i = 0; i < PER; ++i) out[i] = (__bf16)(o[i] * inv);
   }
   if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
+  // device-position decode: advance the position for the next step (the
+  // decode launch that read it has completed before this launch started)
+  if (p.pos_inc != nullptr && row == 0 && lane == 0) *p.pos_inc += 1;
 }
 
 }  // namespace

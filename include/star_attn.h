@@ -374,6 +374,39 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
                      void* stream);
 
 /*
+ * star_decode_step with the token's position in device memory, so that one
+ * recorded sequence of launches (a captured HIP graph) serves every
+ * generated token: the host arguments stay the same from step to step.
+ * Each generated token attends globally to every cached token (Pith review
+ * of Star Attention, "Core claim"); the step is star_decode_step's at
+ * slot = pos = *pos, read at the start of the step, and the step's second
+ * launch (the merge) then adds one to *pos.
+ *   pos               device int64, 8-byte aligned.  When the step runs,
+ *                     part_offsets[P - 1] <= *pos < part_offsets[P] must
+ *                     hold; the last partition then ends right after the
+ *                     token (rows *pos + 1 .. are never read).  For any
+ *                     other value the step writes no cache row, its
+ *                     outputs are o = 0 and lse = -inf, and *pos is still
+ *                     advanced.
+ *   part_offsets      host int64 [P + 1]: partition starts, and in
+ *                     part_offsets[P] the end bound of the positions this
+ *                     call may be replayed at (<= S).  The split chunks of
+ *                     the last partition follow its current length.
+ *   Other arguments, workspaces and errors are star_decode_step's, except
+ *   STAR_ERR_NULL for pos == NULL, STAR_ERR_ALIGN for a misaligned pos,
+ *   and STAR_ERR_SHAPE when part_offsets[P - 1] >= part_offsets[P].
+ *   No allocation; two launches on `stream` and nothing on the host that
+ *   depends on the position, so the call can be captured.  Steps that share
+ *   *pos must run in order on one stream.
+ */
+int star_decode_step_devpos(const star_tensor* q_new, const star_tensor* k_new,
+                            const star_tensor* v_new, const star_tensor* k_cache,
+                            const star_tensor* v_cache, int64_t* pos, double base,
+                            int32_t rope, const int64_t* part_offsets, int32_t P,
+                            int32_t splits, float scale, float* o_part, float* lse_part,
+                            const star_tensor* o, float* lse, void* stream);
+
+/*
  * star_decode_step for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same call without the o_part / lse_part workspaces.  The

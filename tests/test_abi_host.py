@@ -366,3 +366,31 @@ def test_decode_step_noalloc_validation(lib):
                                         5e5, 1, arr, 128, 8, 0.1, ctypes.byref(o64), None,
                                         None) == -5
     assert _lib.STAR_NOALLOC_SCRATCH_BYTES == 4 << 20
+
+
+def test_decode_step_devpos_validation(lib):
+    """The device-position decode step checks everything star_decode_step
+    checks except the position itself (read on the device), plus its
+    pointer: NULL, misaligned, and a last partition that can hold no token."""
+    qn = T(B=1, H=8, S=1, D=128)
+    kn, vn = T(B=1, H=2, S=1, D=128), T(B=1, H=2, S=1, D=128)
+    kc, vc = T(B=1, H=2, S=100, D=128), T(B=1, H=2, S=100, D=128)
+    o = T(B=1, H=8, S=1, D=128, dtype=1)
+
+    def dp(q=qn, oo=o, pos=FAKE, offs=(0, 40, 100), splits=2, op=FAKE, base=5e5):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        return lib.star_decode_step_devpos(ctypes.byref(q), ctypes.byref(kn), ctypes.byref(vn),
+                                           ctypes.byref(kc), ctypes.byref(vc), pos, base, 1, arr,
+                                           len(offs) - 1, splits, 0.1, op, FAKE,
+                                           ctypes.byref(oo), None, None)
+    assert dp(pos=None) == -1
+    assert dp(pos=FAKE + 4) == -4
+    assert dp(offs=(0, 40, 40)) == -2          # the last partition holds no position
+    assert dp(offs=(0, 40, 101)) == -2         # past the cache
+    assert dp(offs=(0, 60, 50)) == -2
+    assert dp(q=T(B=1, H=8, S=2, D=128)) == -2
+    assert dp(oo=T(B=1, H=8, S=2, D=128)) == -2
+    assert dp(q=T(B=1, H=8, S=1, D=128, dtype=1)) == -3
+    assert dp(op=None) == -1
+    assert dp(splits=0) == -2
+    assert dp(base=1.0) == -2
