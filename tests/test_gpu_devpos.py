@@ -170,3 +170,34 @@ def test_devpos_out_of_range_positions():
         assert int(pos.item()) == p0 + 1
         assert bool((o == 0).all()) and bool(torch.isneginf(l).all())
         assert torch.equal(kc, to_dev(k)) and torch.equal(vc, to_dev(v))
+
+
+def test_devpos_never_reads_past_the_token():
+    """The last partition ends right after the device-side position: cache
+    rows past the token hold NaN and +-Inf patterns, and every step still
+    gives star_decode_step's bits (computed with zero rows there)."""
+    case = CASES[0]
+    B, Hq, Hkv, D, L, b, splits, n, rope = case
+    base = 500000.0
+    k, v, steps, offs = setup(case, 70)
+    r_o, r_l, _, _ = reference(case, k, v, steps, offs, base)
+    poison = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFC1], dtype=np.uint16)   # NaN, +Inf, -Inf, NaN
+    kp, vp = k.copy(), v.copy()
+    S = k.shape[2]
+    kp[:, :, L:] = np.resize(poison, (B, Hkv, S - L, D))
+    vp[:, :, L:] = np.resize(poison[::-1], (B, Hkv, S - L, D))
+    kc, vc = to_dev(kp), to_dev(vp)
+    P = len(offs) - 1
+    op = torch.empty((P * splits, B, Hq, 1, D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((P * splits, B, Hq, 1), dtype=torch.float32, device="cuda")
+    pos = torch.tensor([L], dtype=torch.int64, device="cuda")
+    for t in range(n):
+        print(f"devpos poison: step {t}", flush=True)
+        o = torch.full((B, Hq, 1, D), float("nan"), dtype=torch.float32, device="cuda")
+        l = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        sl = slice(t, t + 1)
+        sa.decode_step_devpos(to_dev(steps["q"][:, :, sl]), to_dev(steps["k"][:, :, sl]),
+                              to_dev(steps["v"][:, :, sl]), kc, vc, pos, offs, splits, op, lp,
+                              o, l, base=base, rope=rope)
+        torch.cuda.synchronize()
+        assert torch.equal(o, r_o[t]) and torch.equal(l, r_l[t]), f"step {t} differs"

@@ -23,9 +23,12 @@ def log(msg):
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
 
 
-def test_rmsnorm_parity():
-    x = rand_tensor(61, 0, 1, 1, 300, 4096)[0, 0]
-    g = rand_tensor(61, 1, 1, 1, 1, 4096, 0.5)[0, 0, 0]
+@pytest.mark.parametrize("rows,D", [(300, 4096), (77, 512), (50, 8192), (40, 1000)])
+def test_rmsnorm_parity(rows, D):
+    """The register-resident kernel (D = 512 .. 8192, powers of two) and the
+    general one (D = 1000)."""
+    x = rand_tensor(61, 0, 1, 1, rows, D)[0, 0]
+    g = rand_tensor(61, 1, 1, 1, 1, D, 0.5)[0, 0, 0]
     y = sa.rmsnorm(to_dev(x), to_dev(g), RMS_EPS)
     torch.cuda.synchronize()
     ref = so.rmsnorm(f64(x), f64(g), RMS_EPS)
