@@ -96,7 +96,28 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeParams p, int hgrou
     for (int i = 0; i < 8; ++i) rope_cs(pos, p.inv_freq[8 * ch + i], cs[i], sn[i]);
     const T* xb = reinterpret_cast<const T*>(p.x.data) + (int64_t)b * p.x.sB + s * p.x.sS;
     T* yb = reinterpret_cast<T*>(p.y) + (int64_t)b * p.ysB + s * p.ysS;
-    for (int h = h0; h < h1; ++h) {
+    // heads in groups of HG: all of a group's loads go out before the first
+    // rotation, so a thread keeps 2 HG loads in flight rather than 2
+    constexpr int HG = 4;
+    int h = h0;
+    for (; h + HG <= h1; h += HG) {
+      float x1[HG][8], x2[HG][8];
+#pragma unroll
+      for (int u = 0; u < HG; ++u) {
+        const T* xr = xb + (int64_t)(h + u) * p.x.sH;
+        load8<T>(xr + 8 * ch, x1[u]);
+        load8<T>(xr + half + 8 * ch, x2[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < HG; ++u) {
+        T* yr = yb + (int64_t)(h + u) * p.ysH;
+        double y1[8], y2[8];
+        rotate8(x1[u], x2[u], cs, sn, y1, y2);
+        store8<T>(yr + 8 * ch, y1);
+        store8<T>(yr + half + 8 * ch, y2);
+      }
+    }
+    for (; h < h1; ++h) {
       const T* xr = xb + (int64_t)h * p.x.sH;
       T* yr = yb + (int64_t)h * p.ysH;
       float x1[8], x2[8];
