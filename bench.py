@@ -639,6 +639,19 @@ def trace_summary(root: str) -> str:
     for (n, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{n:60s} {wg:10d} {len(v):6d} {statistics.mean(v):10.2f} "
                      f"{statistics.median(v):10.2f} {min(v):10.2f} {100 * sum(v) / tot:5.1f}%")
+    stats = glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines += ["", "rocprofv3 --stats (one line per kernel name: every grid size together)",
+                  f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+        for f in stats:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    try:
+                        lines.append(f"{_short_kernel_name(r['Name'])[:60]:60s} {int(r['Calls']):6d} "
+                                     f"{float(r['AverageNs']) / 1e3:10.2f} "
+                                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+                    except (KeyError, ValueError):
+                        continue
     return "\n".join(lines)
 
 
