@@ -373,6 +373,7 @@ def decode_graph(st, w, ev, n):
             one()
     out = {}
     for name, graph, replays in (("one_step", g1, n), ("sequence", gn, 1)):
+        pos.fill_(p0)
         graph.replay()                              # untimed first replay
         pos.fill_(p0)
         torch.cuda.synchronize()
