@@ -176,7 +176,7 @@ const char* star_status_string(int status) {
   }
 }
 
-int star_abi_version(void) { return 400; }
+int star_abi_version(void) { return 500; }
 
 int star_rope_freqs(int64_t D, double base, double* inv_freq) {
   if (inv_freq == nullptr) return STAR_ERR_NULL;

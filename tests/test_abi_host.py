@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(lib, s), s
-    assert lib.star_abi_version() == 400
+    assert lib.star_abi_version() == 500
 
 
 def test_status_strings(lib):
