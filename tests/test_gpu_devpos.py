@@ -105,17 +105,21 @@ def test_devpos_eager_equals_decode_step(ci):
                 check_lse(got_l[bb, h:h + 1], rl, f"devpos LSE b{bb} h{h}")
 
 
-@pytest.mark.parametrize("ci", [0, 1])
+# the 8B-128K decode shape (8 partitions x 4 chunks x 8 KV heads = 256 workgroups)
+FULL = (1, 32, 8, 128, 131072, 16384, 4, 3, True)
+
+
+@pytest.mark.parametrize("ci", [0, 1, "full"])
 def test_devpos_graph_replays(ci):
     """One step captured in a HIP graph, replayed once per token with the
     token's inputs copied into the captured buffers in between (eager work
     and a synchronisation between replays): every replay equals
     star_decode_step at that position."""
-    case = CASES[ci]
+    case = FULL if ci == "full" else CASES[ci]
     B, Hq, Hkv, D, L, b, splits, n, rope = case
     print(f"devpos graph: case {case}", flush=True)
     base = 500000.0
-    k, v, steps, offs = setup(case, 50 + ci)
+    k, v, steps, offs = setup(case, 50 + (9 if ci == "full" else ci))
     r_o, r_l, r_k, r_v = reference(case, k, v, steps, offs, base)
     P = len(offs) - 1
     kc, vc = to_dev(k), to_dev(v)
