@@ -75,6 +75,15 @@ def pmc_traffic():
     return float(t.group(1)) if m.group(1) == cur else None
 
 
+def _blas_threads() -> int:
+    """Threads the host BLAS uses (the oracle's matmuls run there)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, x, heads: int = 4, rows_per_call: int = 4096):
     """Time the CPU oracle (as it stands) on a bounded sample of Phase 1:
     every row of block 2 (anchor plus its causal prefix) for the first
@@ -87,11 +96,7 @@ def cpu_baseline(w, x, heads: int = 4, rows_per_call: int = 4096):
 
     import oracle.star_oracle as so
     from workloads import as_f64
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _blas_threads()
     scale = 1.0 / math.sqrt(w.D)
     blk = 1 if w.L > w.b else 0
     s = blk * w.b
@@ -558,24 +563,77 @@ def hbm_stream(ev, mib=1024, reps=5):
             "note": "star_stream_read over 1 GiB (a plain streaming read, 16-byte nontemporal loads)"}
 
 
-def cpu_full_oracle():
-    """The whole oracle (Phase 1 over every row and head, the query rows and
-    every decode step) on the two workloads small enough for it: tiny and
-    llama8b-16k.  (At 8B-128K the oracle's explicit score matrices hold
-    ~7e13 fp64 products, about ten minutes of host time, so the default
-    cpu_baseline times a bounded sample instead.)"""
+FULL_ORACLE = ("tiny", "llama8b-16k", "llama8b-128k", "llama70b-64k", "llama8b-1m")
+
+
+def cpu_full_oracle(names=FULL_ORACLE):
+    """Whole-oracle CPU timings (the oracle as it stands, fp64 numpy, on the
+    host's BLAS threads); only the oracle calls are timed, not the input
+    draws.
+      tiny, llama8b-16k: one call over the whole workload.
+      llama8b-128k, llama70b-64k: one (batch, KV head) group at a time, so
+        that memory stays bounded and progress shows: the oracle's heads are
+        independent and each group's inputs are the workload's own slices,
+        so the groups together are the whole workload (RoPE, Phase 1, the
+        query, every decode step).
+      llama8b-1m: Phase 1 only, extrapolated: blocks 1 and 2 of every head
+        are timed, and each later block costs what block 2 does (the anchor
+        plus a causal block of the same size)."""
+    import dataclasses
+
     import numpy as np
 
     import oracle.star_oracle as so
-    from workloads import WORKLOADS, as_f64, inputs
+    from workloads import WORKLOADS, as_f64, draw_rows, f32_to_bf16_bits, group_inputs, inputs
+    from workloads import T_K, T_Q, T_V
     out = {}
-    for name in ("tiny", "llama8b-16k"):
+    for name in names:
         w = WORKLOADS[name]
-        x = {n: as_f64(t) for n, t in inputs(w, as_bf16=True).items()}
-        t0 = time.perf_counter()
-        so.star_attention(w, x)
-        dt = time.perf_counter() - t0
-        out[name] = {"seconds": dt, "context_tokens_per_s": w.B * w.L / dt,
+        if name == "llama8b-1m":
+            scale = 1.0 / math.sqrt(w.D)
+            rows = 2 * w.b
+            f64 = lambda tid, b, h: as_f64(f32_to_bf16_bits(
+                draw_rows(w.seed, tid, b, h, w.L, w.D, w.scale, 0, rows)))
+            t_blocks = [0.0, 0.0]
+            for b in range(w.B):
+                for kvh in range(w.Hkv):
+                    k, v = f64(T_K, b, kvh), f64(T_V, b, kvh)
+                    qs = [f64(T_Q, b, h) for h in range(kvh * w.g, (kvh + 1) * w.g)]
+                    for blk in (0, 1):
+                        t0 = time.perf_counter()
+                        pos_k = np.arange(rows)
+                        K = so.round_bf16(so.rope(k, pos_k, w.base))
+                        for q in qs:
+                            for r0 in range(blk * w.b, (blk + 1) * w.b, 4096):
+                                pos = np.arange(r0, r0 + 4096)
+                                qr = so.round_bf16(so.rope(q[pos], pos, w.base))
+                                so.phase1_rows(qr, pos, K, v, w.b, w.a, scale)
+                        t_blocks[blk] += time.perf_counter() - t0
+                    progress(f"oracle {name}: blocks 1-2 of group b{b} kv{kvh} done")
+            total = t_blocks[0] + (w.n_blocks - 1) * t_blocks[1]
+            out[name] = {"seconds": total, "context_tokens_per_s": w.B * w.L / total,
+                         "note": f"Phase 1 only, extrapolated: blocks 1 and 2 of every head took "
+                                 f"{t_blocks[0]:.1f} s and {t_blocks[1]:.1f} s; "
+                                 f"{w.n_blocks - 2} more blocks at block 2's cost"}
+            continue
+        dt, groups = 0.0, 0
+        if w.B * w.Hkv == 1 or name in ("tiny", "llama8b-16k"):
+            x = {n: as_f64(t) for n, t in inputs(w, as_bf16=True).items()}
+            t0 = time.perf_counter()
+            so.star_attention(w, x)
+            dt, groups = time.perf_counter() - t0, 1
+        else:
+            wg = dataclasses.replace(w, B=1, Hq=w.g, Hkv=1)
+            for b in range(w.B):
+                for kvh in range(w.Hkv):
+                    x = {n: as_f64(t) for n, t in group_inputs(w, b, kvh).items()}
+                    t0 = time.perf_counter()
+                    so.star_attention(wg, x)
+                    dt += time.perf_counter() - t0
+                    groups += 1
+                    progress(f"oracle {name}: group b{b} kv{kvh} done ({dt:.0f} s so far)")
+        progress(f"oracle {name}: {dt:.1f} s")
+        out[name] = {"seconds": dt, "context_tokens_per_s": w.B * w.L / dt, "groups": groups,
                      "note": "fp64 numpy oracle, whole workload incl. RoPE, Phase 1, query "
                              "and every decode step"}
     return out
@@ -683,14 +741,27 @@ def main():
     ap.add_argument("--configs", default=None,
                     help="comma-separated workloads for the per-workload records "
                          "(default: all five)")
-    ap.add_argument("--cpu-full", action="store_true",
-                    help="also time the whole oracle on the tiny and llama8b-16k workloads")
+    ap.add_argument("--cpu-full", nargs="?", const=",".join(FULL_ORACLE), default=None,
+                    metavar="NAMES",
+                    help="also time the whole oracle on these workloads (default: tiny, "
+                         "8B-16K, 8B-128K and 70B-64K whole, 8B-1M Phase 1 extrapolated "
+                         "from two blocks; ~10 minutes each for the large ones on 16 host "
+                         "threads)")
+    ap.add_argument("--cpu-full-only", action="store_true",
+                    help="with --cpu-full: time the oracle only (no GPU work) and print "
+                         "one JSON line")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="print the per-kernel summary of a rocprofv3 --output-format csv "
                          "kernel trace found under DIR, then exit (no GPU)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.cpu_full_only:
+        if not args.cpu_full:
+            ap.error("--cpu-full-only needs --cpu-full")
+        print(json.dumps({"cpu_full_oracle": cpu_full_oracle(args.cpu_full.split(",")),
+                          "cores": _blas_threads()}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "
@@ -820,7 +891,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, x)
         progress("cpu baseline done")
         if args.cpu_full:
-            out["cpu_full_oracle"] = cpu_full_oracle()
+            full = cpu_full_oracle(args.cpu_full.split(","))
+            ref = full.get(w.name)
+            if ref is not None and "extrapolated" not in ref["note"]:
+                ref["oracle_over_gpu_step"] = ref["seconds"] / (ms_step * 1e-3)
+            out["cpu_full_oracle"] = full
     print(json.dumps(out), flush=True)
 
 

@@ -75,3 +75,19 @@ def test_anchor_positions_precede_their_block():
         p = pos[i]
         assert p.size == a and np.all(np.diff(p) > 0) and p.min() >= 0 and p.max() < i * b
     assert all(np.array_equal(x, y) for x, y in zip(pos, anchor_positions(3, L, b, a)))
+
+
+def test_group_inputs_are_the_workload_slices():
+    """One (batch, KV head) group's tensors equal the matching slices of the
+    whole workload's draws: KV head kvh and query heads kvh*g .. kvh*g+g-1."""
+    import dataclasses
+    from workloads import group_inputs, inputs
+    w = dataclasses.replace(WORKLOADS["llama8b-16k"], name="small", B=2, Hq=8, Hkv=2, L=4100,
+                            b=1024, Lq=5, T=3)
+    full = inputs(w)
+    for b in range(w.B):
+        for kvh in range(w.Hkv):
+            grp = group_inputs(w, b, kvh)
+            for name, t in grp.items():
+                hs = slice(kvh * w.g, (kvh + 1) * w.g) if name.startswith("q") else slice(kvh, kvh + 1)
+                assert np.array_equal(t, full[name][b:b + 1, hs]), (name, b, kvh)

@@ -196,6 +196,28 @@ def inputs(w: Workload, as_bf16: bool = True) -> dict:
             for name, (tid, H, S) in spec.items()}
 
 
+def group_inputs(w: Workload, b: int, kvh: int, as_bf16: bool = True) -> dict:
+    """The tensors of one (batch, KV head) group: KV head ``kvh`` of batch
+    ``b`` and its g query heads, every slice drawn exactly as :func:`inputs`
+    draws it (same seeds), with shapes [1, g, S, D] (query heads) and
+    [1, 1, S, D] (the KV head)."""
+    g = w.g
+    spec = {
+        "q": (T_Q, True, w.L), "k": (T_K, False, w.L), "v": (T_V, False, w.L),
+        "qq": (T_QQ, True, w.Lq), "kq": (T_KQ, False, w.Lq), "vq": (T_VQ, False, w.Lq),
+        "qd": (T_QD, True, w.T), "kd": (T_KD, False, w.T), "vd": (T_VD, False, w.T),
+    }
+    out = {}
+    for name, (tid, is_q, S) in spec.items():
+        heads = range(kvh * g, (kvh + 1) * g) if is_q else [kvh]
+        arr = np.empty((1, len(heads), S, w.D), dtype=np.uint16 if as_bf16 else np.float32)
+        for i, h in enumerate(heads):
+            x = draw_rows(w.seed, tid, b, h, S, w.D, w.scale)
+            arr[0, i] = f32_to_bf16_bits(x) if as_bf16 else x
+        out[name] = arr
+    return out
+
+
 def as_f64(t: np.ndarray) -> np.ndarray:
     """Exact float64 view of a tensor from ``inputs`` (bf16 bits or fp32)."""
     if t.dtype == np.uint16:
