@@ -124,6 +124,18 @@ def cpu_baseline(w, x, heads: int = 4, rows_per_call: int = 4096):
                        f"{total_pairs:.3e}")}
 
 
+def pages_host_pairs(L: int, b: int, a: int) -> int:
+    """(query, key) pairs per head as the pages' hosts compute them: host 1
+    runs causal attention over its block, host i >= 2 over its augmented
+    block [anchor ; block i] of a + n_i tokens, the anchor's rows included
+    (one GPU skips those rows, so they are not in the useful count)."""
+    tot = 0
+    for i, s in enumerate(range(0, L, b)):
+        m = min(s + b, L) - s + (a if i > 0 else 0)
+        tot += m * (m + 1) // 2
+    return tot
+
+
 def prefix_pairs(L: int, b: int, lens) -> int:
     """Useful (query, key) pairs per head of Phase 1 with a per-block prefix
     of lens[i] keys: every row sees its block's prefix and its causal
@@ -848,7 +860,11 @@ def main():
                    "kernel_min_ms": float(np.min(p1_samples)), "rope_ms": rope_ms,
                    "context_tokens_per_s": w.B * w.L / (p1_ms * 1e-3),
                    "context_tokens_per_s_with_rope": w.B * w.L / ((p1_ms + rope_ms) * 1e-3),
-                   "tflops": p1_tflops, "algorithmic_flops": flops},
+                   "tflops": p1_tflops, "algorithmic_flops": flops,
+                   "pages_host_flops": 4 * w.D * w.Hq * w.B * pages_host_pairs(w.L, w.b, w.a),
+                   "note": "algorithmic_flops counts useful (query, key) pairs; "
+                           "pages_host_flops is the pages' per-host count (every host also "
+                           "recomputes its anchor rows), for information"},
         "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
                      "traffic": pmc_traffic(),

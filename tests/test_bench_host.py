@@ -106,3 +106,20 @@ def test_short_kernel_names():
              "long, unsigned int*)") == "star::stream_read_kernel"
     assert f("void star::(anonymous namespace)::merge_kernel<128>(star::MergeParams)") == \
         "star::merge_kernel<128>"
+
+
+def test_pages_host_flops():
+    """The pages' per-host count (causal over the 2b-token augmented block,
+    anchor rows included): 6.38e13 FLOP at 8B-128K, and a brute-force count
+    on a small ragged case."""
+    bench = load_bench()
+    from workloads import WORKLOADS
+    w = WORKLOADS["llama8b-128k"]
+    assert 4 * w.D * w.Hq * w.B * bench.pages_host_pairs(w.L, w.b, w.a) == pytest.approx(6.38e13, rel=1e-3)
+    L, b, a = 23, 7, 7
+    brute = 0
+    for s in range(0, L, b):
+        n = min(s + b, L) - s
+        m = n + (a if s > 0 else 0)
+        brute += sum(r + 1 for r in range(m))
+    assert bench.pages_host_pairs(L, b, a) == brute
