@@ -43,10 +43,12 @@ def partition_offsets(L: int, b: int, cache_len: int):
 
 
 def choose_splits(B: int, Hkv: int, P: int, part_len: int, target_wg: int,
-                  min_chunk: int) -> int:
-    """Chunks per partition so that B*Hkv*P*splits workgroups fill the chip
-    without cutting chunks below ``min_chunk`` keys."""
-    want = max(1, math.ceil(target_wg / max(1, B * Hkv * P)))
+                  min_chunk: int, row_groups: int = 1) -> int:
+    """Chunks per partition so that B*Hkv*P*splits*row_groups workgroups
+    fill the chip without cutting chunks below ``min_chunk`` keys
+    (``row_groups``: workgroups per chunk, one per 256 query rows of a KV
+    head in the flash kernel)."""
+    want = max(1, math.ceil(target_wg / max(1, B * Hkv * P * row_groups)))
     cap = max(1, math.ceil(part_len / min_chunk))
     return int(min(want, cap, 1024))
 
@@ -82,7 +84,10 @@ class StarAttentionStep:
         part_len = min(b, L)
         # query chunks: one workgroup per CU (256 at 8B-128K) -- measured
         # 164 us against 190 us for two rounds of half-length chunks
-        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 256, 512)
+        g = Hq // Hkv
+        rows = g * max(Lq, 1)
+        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 256, 512,
+                                                1 if rows <= 16 else math.ceil(rows / 256))
         self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 256, 512)
         nq = self.P * self.sq
         nd = self.P * self.sd
