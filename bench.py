@@ -12,9 +12,17 @@ Prints ONE JSON line.  ``value`` is whole-step context tokens/s
 (B*L per step / step time).  ``phase1`` / ``decode`` hold the per-phase
 rates; ``roofline`` is for the dominant kernel (the Phase-1 flash kernel,
 bf16 MFMA), timed with HIP events on the stream it is launched on;
-``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample.
+``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample.  Beside
+them: ``decode_cold`` (each step after a cache-flushing read),
+``decode_graph`` (steps replayed from captured HIP graphs),
+``phase2_query`` (the query partials against their roofline),
+``hbm_stream`` (the streaming-read reference), ``phase1_variants``,
+``phase1_layer`` and ``per_config`` (one record per workload with the errors
+of a sampled parity check against the oracle).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --cpu-full [NAMES] [--cpu-full-only]   # whole-oracle timings
+    python bench.py --trace-summary DIR                    # rocprofv3 csv -> table
 """
 from __future__ import annotations
 
