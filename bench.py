@@ -360,58 +360,41 @@ def phase2_query(st, w, ev, in_step_ms, reps=20):
 
 
 def decode_graph(st, w, ev, n):
-    """Decode steps replayed from captured HIP graphs (star_decode_step_devpos
-    and its merge: the token's position lives in device memory and each
-    step advances it), against the eager steps whose host-side launch work
-    can exceed a short step's GPU time.
-      one_step: a graph of one step, replayed ``n`` times back to back;
-        each replay also pays the runtime's gap between graph launches.
+    """Decode steps replayed from captured HIP graphs (pipeline.DecodeGraph:
+    star_decode_step_devpos and its merge, the position in device memory),
+    against the eager steps whose host-side launch work can exceed a short
+    step's GPU time.
       sequence: ``n`` consecutive steps captured in one graph and replayed
         once, as a per-token graph of a model with ``n`` attention layers
-        would hold them: the launch gap is paid once.
+        would hold them: the runtime's gap between graph launches is paid
+        once.
+      one_step: a graph of one step, replayed ``n`` times back to back.
     Writes cache rows L + Lq .. L + Lq + n - 1, as the timed steps do."""
     import numpy as np
     import torch
 
-    from block_sparse_amd import decode_step_devpos
-    from block_sparse_amd.pipeline import partition_offsets
+    from block_sparse_amd.pipeline import DecodeGraph
     p0 = w.L + w.Lq
-    offs = partition_offsets(w.L, w.b, st.S)       # positions up to the cache's end
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
-    mk = lambda H: torch.randn((w.B, H, 1, w.D), device="cuda", generator=gen).to(torch.bfloat16)
-    qb, kb, vb = mk(w.Hq), mk(w.Hkv), mk(w.Hkv)
-    ob = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device="cuda")
-    lb = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    pos = torch.full((1,), p0, dtype=torch.int64, device="cuda")
-
-    def one():
-        decode_step_devpos(qb, kb, vb, st.kc, st.vc, pos, offs, st.sd, st.op_d, st.lp_d, ob, lb,
-                           base=w.base, rope=w.rope, scale=st.scale)
-
-    torch.cuda.synchronize()
-    g1, gn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g1):
-        one()
-    with torch.cuda.graph(gn):
-        for _ in range(n):
-            one()
     out = {}
-    for name, graph, replays in (("one_step", g1, n), ("sequence", gn, 1)):
-        pos.fill_(p0)
-        graph.replay()                              # untimed first replay
-        pos.fill_(p0)
+    for name, steps, replays in (("one_step", 1, n), ("sequence", n, 1)):
+        dg = DecodeGraph(st, p0, steps)
+        for t in (dg.q_in, dg.k_in, dg.v_in):
+            t.copy_(torch.randn(t.shape, device="cuda", generator=gen))
+        dg.replay()                                 # untimed first replay
+        dg.set_position(p0)
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         e0.record()
         for _ in range(replays):
-            graph.replay()
+            dg.replay()
         e1.record()
         torch.cuda.synchronize()
-        if int(pos.item()) != p0 + n:
+        if int(dg.pos.item()) != p0 + n:
             raise RuntimeError("device position did not advance once per step")
         out[name] = e0.elapsed_time(e1) / n
-    del g1, gn
+        del dg
     byts = float(np.mean([decode_bytes(w, t) for t in range(n)]))
     ms = out["sequence"]
     return {"us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,

@@ -31,9 +31,9 @@ import math
 
 import torch
 
-from . import (decode_prepare, decode_step, gather_rows, kv_append, lse_merge,
-               phase1_blocklocal, phase1_prefix, phase1_rope, phase2_partial, pulsar_prefix,
-               rope_apply, sched_workspace)
+from . import (decode_prepare, decode_step, decode_step_devpos, gather_rows, kv_append,
+               lse_merge, phase1_blocklocal, phase1_prefix, phase1_rope, phase2_partial,
+               pulsar_prefix, rope_apply, sched_workspace)
 
 
 def partition_offsets(L: int, b: int, cache_len: int):
@@ -241,3 +241,47 @@ class StarAttentionStep:
         self.query(qq, kq, vq)
         for t in range(self.T):
             self.decode(t, qd[:, :, t:t + 1], kd[:, :, t:t + 1], vd[:, :, t:t + 1])
+
+
+class DecodeGraph:
+    """Decode steps replayed from one captured HIP graph
+    (star_decode_step_devpos): the token's position lives in device memory
+    (``pos``) and every step advances it, so the graph's arguments never
+    change.  ``steps`` consecutive steps are captured together (a per-token
+    graph of a model would hold one step per attention layer; each graph
+    launch costs the runtime a gap of a few microseconds).
+
+    Before each :meth:`replay`, write the next tokens' un-rotated q/k/v into
+    ``q_in``, ``k_in``, ``v_in`` ([B, H, steps, D]); afterwards ``out`` and
+    ``lse`` ([B, Hq, steps, D] and [steps, B, Hq]) hold their attention
+    outputs.  Positions run from ``first`` to ``st.S - 1``."""
+
+    def __init__(self, st: "StarAttentionStep", first: int, steps: int = 1):
+        if not (st.L <= first and first + steps <= st.S):
+            raise ValueError("positions outside the cache")
+        B, Hq, Hkv, D = st.B, st.Hq, st.Hkv, st.D
+        dev = st.kc.device
+        bf = torch.bfloat16
+        self.st, self.first, self.steps = st, first, steps
+        self.q_in = torch.zeros((B, Hq, steps, D), dtype=bf, device=dev)
+        self.k_in = torch.zeros((B, Hkv, steps, D), dtype=bf, device=dev)
+        self.v_in = torch.zeros((B, Hkv, steps, D), dtype=bf, device=dev)
+        self.out = torch.empty((B, Hq, steps, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((steps, B, Hq), dtype=torch.float32, device=dev)
+        self.pos = torch.full((1,), first, dtype=torch.int64, device=dev)
+        offs = partition_offsets(st.L, st.b, st.S)     # the last partition may grow to S
+        torch.cuda.synchronize(dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(steps):
+                decode_step_devpos(self.q_in[:, :, i:i + 1], self.k_in[:, :, i:i + 1],
+                                   self.v_in[:, :, i:i + 1], st.kc, st.vc, self.pos, offs,
+                                   st.sd, st.op_d, st.lp_d, self.out[:, :, i:i + 1],
+                                   self.lse[i], base=st.base, rope=st.rope, scale=st.scale)
+
+    def set_position(self, p: int):
+        """Position of the next step (an eager fill, not part of the graph)."""
+        self.pos.fill_(p)
+
+    def replay(self):
+        self.graph.replay()

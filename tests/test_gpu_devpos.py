@@ -205,3 +205,46 @@ def test_devpos_never_reads_past_the_token():
                               o, l, base=base, rope=rope)
         torch.cuda.synchronize()
         assert torch.equal(o, r_o[t]) and torch.equal(l, r_l[t]), f"step {t} differs"
+
+
+def test_decode_graph_helper():
+    """pipeline.DecodeGraph: 3 steps per graph, replayed twice with new
+    inputs written in between, equals 6 eager star_decode_step calls bit for
+    bit (outputs, lse and the cache)."""
+    from block_sparse_amd.pipeline import DecodeGraph, StarAttentionStep
+    B, Hq, Hkv, D, L, b, splits = 1, 16, 4, 128, 2500, 1024, 3
+    n, per = 6, 3
+    print(f"decode graph helper: L={L} steps={n}", flush=True)
+    q = rand_tensor(80, 0, B, Hq, L, D)
+    k = rand_tensor(80, 1, B, Hkv, L, D)
+    v = rand_tensor(80, 2, B, Hkv, L, D)
+    qd, kd, vd = (rand_tensor(80, t, B, H, n, D) for t, H in ((6, Hq), (7, Hkv), (8, Hkv)))
+    runs = []
+    for use_graph in (False, True):
+        st = StarAttentionStep(B, Hq, Hkv, D, L, b, 0, n, splits_decode=splits)
+        st.load_context(to_dev(v))
+        st.rope_context(to_dev(q), to_dev(k))
+        if not use_graph:
+            for t in range(n):
+                sl = slice(t, t + 1)
+                st.decode(t, to_dev(qd[:, :, sl]), to_dev(kd[:, :, sl]), to_dev(vd[:, :, sl]))
+            torch.cuda.synchronize()
+            runs.append((st.od.clone(), st.lsed.clone(), st.kc.clone(), st.vc.clone()))
+            continue
+        dg = DecodeGraph(st, L, per)
+        od = torch.empty_like(st.od)
+        ld = torch.empty_like(st.lsed)
+        for r in range(n // per):
+            sl = slice(r * per, (r + 1) * per)
+            dg.q_in.copy_(to_dev(qd[:, :, sl]))
+            dg.k_in.copy_(to_dev(kd[:, :, sl]))
+            dg.v_in.copy_(to_dev(vd[:, :, sl]))
+            dg.replay()
+            torch.cuda.synchronize()
+            od[:, :, sl] = dg.out
+            ld[sl] = dg.lse
+        assert int(dg.pos.item()) == L + n
+        runs.append((od, ld, st.kc.clone(), st.vc.clone()))
+    (o0, l0, k0, v0), (o1, l1, k1, v1) = runs
+    assert torch.equal(o0, o1) and torch.equal(l0, l1), "graph steps differ from eager ones"
+    assert torch.equal(k0, k1) and torch.equal(v0, v1), "cache differs"
