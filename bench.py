@@ -125,7 +125,7 @@ def cpu_baseline(w, x, heads: int = 4, rows_per_call: int = 4096):
     total_pairs = phase1_pairs(w.L, w.b, w.a) * w.Hq * w.B
     tokens_per_s = w.B * w.L / (dt * total_pairs / sample_pairs)
     return {"value": tokens_per_s, "unit": "context tokens/s (Phase 1, extrapolated)",
-            "cores": int(cores), "kind": "oracle",
+            "cores": int(cores), "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": (f"fp64 numpy oracle, Phase 1 of all {e - s} rows of block {blk + 1} "
                        f"(positions {s}-{e - 1}) for {heads} query heads of KV head 0, incl. "
                        f"RoPE; {dt:.1f} s; scaled by useful (q,k) pairs {sample_pairs:.3e} of "
@@ -495,6 +495,7 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
     err = {"phase1_max_abs": 0.0, "phase1_mean_abs": 0.0, "phase1_lse": 0.0,
            "query_max_abs": 0.0, "query_lse": 0.0, "decode_max_abs": 0.0, "decode_lse": 0.0}
     ok = True
+    oracle_p2 = 0.0
     for h in range(g):
         rw, rl = so.phase1_rows(rot(host["q"][h][pos], pos), pos, K, Vw, w.b, w.a, scale)
         ro, wabs = rw[:, :w.D], rw[:, w.D:]
@@ -506,7 +507,9 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
         err["phase1_mean_abs"] = max(err["phase1_mean_abs"], float(d.mean()))
         err["phase1_lse"] = max(err["phase1_lse"], float(np.abs(gl - rl).max()))
         rows = np.concatenate([rot(host["qq"][h], pq), rot(host["qd"][h], pd)])
+        t_p2 = time.perf_counter()
         o, l, _, _ = so.phase2(rows, np.concatenate([pq, pd]), Kc, Vc, parts, scale)
+        oracle_p2 += time.perf_counter() - t_p2
         if w.Lq:
             err["query_max_abs"] = max(err["query_max_abs"], float(np.abs(
                 st.o2[0, h].cpu().numpy() - o[:w.Lq]).max()))
@@ -524,6 +527,9 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
                      "phase1_rows_per_head": int(pos.size), "query_rows": w.Lq,
                      "decode_steps": n_dec,
                      "checked": "batch 0, KV head 0 and its query heads, vs the fp64 oracle"}
+    if w.Lq + n_dec:
+        # the oracle's merged Phase-2 attention per token, every head
+        rec["oracle_phase2_ms_per_token"] = (oracle_p2 / (g * (w.Lq + n_dec)) * w.B * w.Hq * 1e3)
     if n_dec:
         # after the parity check: the replays overwrite the decode rows
         gr = decode_graph(st, w, ev, n_dec)
@@ -567,6 +573,22 @@ def hbm_stream(ev, mib=1024, reps=5):
 
 
 FULL_ORACLE = ("tiny", "llama8b-16k", "llama8b-128k", "llama70b-64k", "llama8b-1m")
+
+
+def oracle_flops(w, blocks=None) -> float:
+    """fp64 FLOPs the oracle executes for Phase 1 (its explicit masks make
+    every block a full rectangle: n_i rows x (n_i or a + n_i) keys, QK^T and
+    PV) and for Phase 2 (every query and decode row over its cache), all
+    heads.  ``blocks``: count only the first ``blocks`` blocks' Phase 1."""
+    per_head = 0
+    for i, s0 in enumerate(range(0, w.L, w.b)):
+        if blocks is not None and i >= blocks:
+            break
+        n = min(s0 + w.b, w.L) - s0
+        per_head += 4 * w.D * n * (n + (w.a if i > 0 else 0))
+    if blocks is None:
+        per_head += 4 * w.D * (w.Lq * (w.L + w.Lq) + sum(w.L + w.Lq + t + 1 for t in range(w.T)))
+    return float(per_head * w.Hq * w.B)
 
 
 def cpu_full_oracle(names=FULL_ORACLE):
@@ -615,6 +637,7 @@ def cpu_full_oracle(names=FULL_ORACLE):
                     progress(f"oracle {name}: blocks 1-2 of group b{b} kv{kvh} done")
             total = t_blocks[0] + (w.n_blocks - 1) * t_blocks[1]
             out[name] = {"seconds": total, "context_tokens_per_s": w.B * w.L / total,
+                         "fp64_gflops": oracle_flops(w, 2) / sum(t_blocks) / 1e9,
                          "note": f"Phase 1 only, extrapolated: blocks 1 and 2 of every head took "
                                  f"{t_blocks[0]:.1f} s and {t_blocks[1]:.1f} s; "
                                  f"{w.n_blocks - 2} more blocks at block 2's cost"}
@@ -637,6 +660,7 @@ def cpu_full_oracle(names=FULL_ORACLE):
                     progress(f"oracle {name}: group b{b} kv{kvh} done ({dt:.0f} s so far)")
         progress(f"oracle {name}: {dt:.1f} s")
         out[name] = {"seconds": dt, "context_tokens_per_s": w.B * w.L / dt, "groups": groups,
+                     "fp64_gflops": oracle_flops(w) / dt / 1e9,
                      "note": "fp64 numpy oracle, whole workload incl. RoPE, Phase 1, query "
                              "and every decode step"}
     return out
@@ -764,7 +788,8 @@ def main():
         if not args.cpu_full:
             ap.error("--cpu-full-only needs --cpu-full")
         print(json.dumps({"cpu_full_oracle": cpu_full_oracle(args.cpu_full.split(",")),
-                          "cores": _blas_threads()}), flush=True)
+                          "cores": _blas_threads(),
+                          "affinity_cores": len(os.sched_getaffinity(0))}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "

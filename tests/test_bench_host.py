@@ -123,3 +123,19 @@ def test_pages_host_flops():
         m = n + (a if s > 0 else 0)
         brute += sum(r + 1 for r in range(m))
     assert bench.pages_host_pairs(L, b, a) == brute
+
+
+def test_oracle_flops_follow_the_oracles_key_sets():
+    """The oracle's executed Phase-1 FLOPs: every block is a full rectangle
+    of its rows by the key set the oracle builds for it."""
+    import dataclasses
+    import oracle.star_oracle as so
+    from workloads import WORKLOADS
+    bench = load_bench()
+    w = dataclasses.replace(WORKLOADS["llama8b-16k"], L=1000, b=300, T=0, Lq=0)
+    per_head = 0
+    for i, (s, e) in enumerate(so.blocks(w.L, w.b)):
+        keys, mask = so.phase1_block_keys(i, w.L, w.b, w.a)
+        per_head += 4 * w.D * mask.shape[0] * mask.shape[1]
+    assert bench.oracle_flops(w) == per_head * w.Hq * w.B
+    assert bench.oracle_flops(w, 2) < bench.oracle_flops(w)
