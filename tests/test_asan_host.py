@@ -1,11 +1,13 @@
-"""The host-side code of the C ABI under AddressSanitizer (CPU only).
+"""The host-side code of the C ABI under AddressSanitizer and
+UndefinedBehaviorSanitizer (CPU only).
 
 The library's host objects -- argument validation and dispatch (abi.cpp),
 the no-allocation entry point's host part (noalloc.hip), Pulsar's Max-IDF
 selection (pulsar.cpp) and the rocBLAS wrapper (blas.cpp) -- are rebuilt
-with AddressSanitizer on their host pass and linked with the normal kernel
-objects.  The ABI tests (every entry point's validation, the Pulsar
-selection against the oracle, the RoPE frequencies) then run against that
+with AddressSanitizer and UndefinedBehaviorSanitizer (undefined behaviour
+aborts) on their host pass and linked with the normal kernel objects.  The
+ABI tests (every entry point's validation, the Pulsar selection against the
+oracle, the RoPE frequencies) then run against that
 build in a child Python process with the sanitizer runtime preloaded
 (Python itself is not instrumented).  A planted overflow -- the Pulsar call
 told that its output holds more rows than it does -- must be reported, so a
@@ -48,13 +50,16 @@ def asan_lib(tmp_path_factory):
         obj = str(out / (name + ".o"))
         cmd = [B.hipcc(), "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={B.ARCH}",
                *B.DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, name), "-o", obj,
-               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+               "-Xarch_host", "-fsanitize=address,undefined",
+               "-Xarch_host", "-fno-sanitize-recover=undefined",
+               "-Xarch_host", "-fno-omit-frame-pointer"]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         objs.append(obj)
     lib = str(out / "libstarattn_asan.so")
     cmd = [B.hipcc(), "-shared", "-fPIC", f"--offload-arch={B.ARCH}", *objs, *kernels, "-o", lib,
-           "-lrocblas", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libasan"]
+           "-lrocblas", "-Xarch_host", "-fsanitize=address,undefined",
+           "-Xarch_host", "-shared-libasan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return lib
@@ -83,6 +88,16 @@ lib.star_pulsar_prefix(tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), L, b,
                        st.ctypes.data_as(P64), ln.ctypes.data_as(P64), 4)
 print("no report", n.value)
 """
+
+
+def test_undefined_behaviour_checks_are_compiled_in(asan_lib):
+    """The host objects carry UndefinedBehaviorSanitizer checks (their
+    handlers are referenced by this build of the library), so the ABI tests
+    below also run under them."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", asan_lib], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "__ubsan_handle_" in r.stdout
+    assert "__asan_" in r.stdout
 
 
 def test_sanitizer_catches_a_planted_overflow(asan_lib):
