@@ -381,7 +381,9 @@ int star_decode_step(const star_tensor* q_new, const star_tensor* k_new,
  * of Star Attention, "Core claim"); the step is star_decode_step's at
  * slot = pos = *pos, read at the start of the step, and the step's second
  * launch (the merge) then adds one to *pos.
- *   pos               device int64, 8-byte aligned.  When the step runs,
+ *   pos               device int64, 8-byte aligned, one position for every
+ *                     sequence of the batch (they decode in lockstep, as
+ *                     with star_decode_step).  When the step runs,
  *                     part_offsets[P - 1] <= *pos < part_offsets[P] must
  *                     hold; the last partition then ends right after the
  *                     token (rows *pos + 1 .. are never read).  For any
