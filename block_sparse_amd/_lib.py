@@ -19,6 +19,7 @@ STAR_F32 = 1
 STAR_MAX_PARTS = 128
 STAR_SPLIT_ALIGN = 64
 STAR_NOALLOC_SCRATCH_BYTES = 4 << 20
+STAR_BLAS_WORKSPACE_BYTES = 64 << 20
 
 STATUS = {
     0: "STAR_OK", -1: "STAR_ERR_NULL", -2: "STAR_ERR_SHAPE", -3: "STAR_ERR_DTYPE",

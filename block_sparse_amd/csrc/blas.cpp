@@ -1,7 +1,8 @@
 // The plain GEMMs around the attention (q/k/v and output projections of the
 // Llama-3 attention block) run in rocBLAS: bf16 operands, fp32 accumulation,
 // bf16 result, with the residual add folded in as beta * C.  A star_context
-// owns the rocBLAS handle, so the library itself keeps no global state.
+// owns the rocBLAS handle and a fixed device workspace handed to it, so the
+// library keeps no global state and a GEMM call never allocates.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -14,6 +15,7 @@
 
 struct star_context {
   rocblas_handle blas;
+  void* workspace;
 };
 
 namespace {
@@ -31,9 +33,23 @@ extern "C" {
 int star_context_create(star_context** ctx) {
   if (ctx == nullptr) return STAR_ERR_NULL;
   *ctx = nullptr;
-  star_context* c = new (std::nothrow) star_context;
+  star_context* c = new (std::nothrow) star_context{nullptr, nullptr};
   if (c == nullptr) return STAR_ERR_UNSUPPORTED;
   if (rocblas_create_handle(&c->blas) != rocblas_status_success) {
+    delete c;
+    return STAR_ERR_BLAS;
+  }
+  // a user-owned workspace: rocBLAS uses it and allocates nothing itself
+  if (hipMalloc(&c->workspace, STAR_BLAS_WORKSPACE_BYTES) != hipSuccess) {
+    c->workspace = nullptr;
+    rocblas_destroy_handle(c->blas);
+    delete c;
+    return STAR_ERR_HIP;
+  }
+  if (rocblas_set_workspace(c->blas, c->workspace, STAR_BLAS_WORKSPACE_BYTES) !=
+      rocblas_status_success) {
+    rocblas_destroy_handle(c->blas);
+    (void)hipFree(c->workspace);
     delete c;
     return STAR_ERR_BLAS;
   }
@@ -44,8 +60,10 @@ int star_context_create(star_context** ctx) {
 int star_context_destroy(star_context* ctx) {
   if (ctx == nullptr) return STAR_OK;
   const rocblas_status s = rocblas_destroy_handle(ctx->blas);
+  const hipError_t e = ctx->workspace != nullptr ? hipFree(ctx->workspace) : hipSuccess;
   delete ctx;
-  return s == rocblas_status_success ? STAR_OK : STAR_ERR_BLAS;
+  if (s != rocblas_status_success) return STAR_ERR_BLAS;
+  return e == hipSuccess ? STAR_OK : STAR_ERR_HIP;
 }
 
 int star_linear(star_context* ctx, const star_tensor* x, const star_tensor* w,

@@ -32,10 +32,10 @@
  *   passed by the caller, normally 1/sqrt(D)).  A row that sees no key has
  *   o = 0 and lse = -inf.
  * - Ownership: the caller allocates and owns every buffer.  No entry point
- *   allocates, frees or synchronises, with two exceptions in the attention
- *   layer's calls: star_context_create allocates the context, and
- *   star_linear runs rocBLAS, which manages its own device workspace (it
- *   may allocate it on a first call).  Work is enqueued on `stream` (a
+ *   allocates, frees or synchronises, with one exception in the attention
+ *   layer's calls: star_context_create allocates the context and its fixed
+ *   rocBLAS workspace (star_context_destroy frees them); star_linear then
+ *   allocates nothing.  Work is enqueued on `stream` (a
  *   hipStream_t passed as void*; NULL = the null stream) and the call returns
  *   without waiting.  The library holds no mutable global state apart from
  *   star_decode_step_noalloc's per-GPU scratch array (see there), so the
@@ -443,10 +443,15 @@ int star_decode_step_noalloc(const star_tensor* q_new, const star_tensor* k_new,
  * Attention, "What carries the argument").
  *
  * The projections are plain GEMMs and run in rocBLAS; a star_context owns
- * the rocBLAS handle.  Create one per thread that issues star_linear calls
- * (star_context_create allocates; it is not a hot call) and destroy it when
- * done.  Calls with one context must not run concurrently from two threads.
+ * the rocBLAS handle and a device workspace of STAR_BLAS_WORKSPACE_BYTES
+ * handed to rocBLAS, so that star_linear never allocates.  Create one per
+ * thread that issues star_linear calls, on the device they will run on
+ * (star_context_create allocates; it is not a hot call: STAR_ERR_HIP if the
+ * workspace cannot be allocated, STAR_ERR_BLAS if rocBLAS fails), and
+ * destroy it when done.  Calls with one context must not run concurrently
+ * from two threads or streams (they share the workspace).
  */
+#define STAR_BLAS_WORKSPACE_BYTES (64 << 20)
 typedef struct star_context star_context;
 
 int star_context_create(star_context** ctx);
