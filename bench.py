@@ -12,8 +12,9 @@ Prints ONE JSON line.  ``value`` is whole-step context tokens/s
 (B*L per step / step time).  ``phase1`` / ``decode`` hold the per-phase
 rates; ``roofline`` is for the dominant kernel (the Phase-1 flash kernel,
 bf16 MFMA), timed with HIP events on the stream it is launched on;
-``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample.  Beside
-them: ``decode_cold`` (each step after a cache-flushing read),
+``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample;
+``phase1.separate_rope`` times the same Phase 1 with the rotation of Q as a
+pass of its own.  Beside them: ``decode_cold`` (each step after a cache-flushing read),
 ``decode_graph`` (steps replayed from captured HIP graphs),
 ``phase2_query`` (the query partials against their roofline),
 ``hbm_stream`` (the streaming-read reference), ``phase1_variants``,
@@ -403,6 +404,43 @@ def decode_graph(st, w, ev, n):
             "note": f"{n} decode steps (star_decode_step_devpos + merge) captured in one HIP "
                     "graph and replayed; one_step_graph: a one-step graph replayed "
                     f"{n} times (each replay adds the runtime's gap between graph launches)"}
+
+
+def phase1_separate_rope(st, dev, w, ev, reps=5):
+    """The same box, interleaved: the step's Phase-1 call (Q rotated inside
+    the kernel) against the rotation of Q as a pass of its own
+    (star_rope_apply) followed by star_phase1_blocklocal on the rotated Q.
+    Both give the same bits; the second kernel does attention only."""
+    import numpy as np
+    import torch
+
+    import block_sparse_amd as sa
+    L = w.L
+    t = {"fused": [], "rope_q": [], "blocklocal": []}
+    for _ in range(reps):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        st.phase1()
+        e[1].record()
+        sa.rope_apply(dev["q"], pos0=0, base=w.base, out=st.qr)
+        e[2].record()
+        sa.phase1_blocklocal(st.qr, st.kc[:, :, :L], st.vc[:, :, :L], st.b, st.a, st.scale,
+                             out=st.o1, lse=st.lse1, sched=st.sched)
+        e[3].record()
+        torch.cuda.synchronize()
+        for k, (a, b) in zip(t, ((0, 1), (1, 2), (2, 3))):
+            t[k].append(e[a].elapsed_time(e[b]))
+    med = {k: float(np.median(v)) for k, v in t.items()}
+    fl = phase1_flops(w)
+    return {"fused_ms": med["fused"], "rope_q_ms": med["rope_q"],
+            "blocklocal_ms": med["blocklocal"],
+            "separate_total_ms": med["rope_q"] + med["blocklocal"],
+            "blocklocal_tflops": fl / (med["blocklocal"] * 1e-3) / 1e12,
+            "blocklocal_frac_of_peak": fl / (med["blocklocal"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "reps": reps,
+            "note": "medians of interleaved launches: star_phase1_rope (the step's call) "
+                    "against star_rope_apply on Q + star_phase1_blocklocal (same output "
+                    "bits; that kernel does attention only)"}
 
 
 def config_record(name, ev, rows_per_block=8, decode_steps=16):
@@ -891,6 +929,9 @@ def main():
                      "traffic": pmc_traffic(),
                      "kernel": "flash2_kernel (Phase 1)"},
     }
+    if st.fuse_q_rope:
+        out["phase1"]["separate_rope"] = phase1_separate_rope(st, dev, w, ev)
+        progress("Phase 1 with the rotation of Q as its own pass done")
     if not args.phase1_only and w.T > 0:
         dec_ms = np.mean([r["dec"][0].elapsed_time(r["dec"][1]) for r in recs])
         byts = sum(decode_bytes(w, t) for t in range(w.T))
