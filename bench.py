@@ -13,8 +13,9 @@ Prints ONE JSON line.  ``value`` is whole-step context tokens/s
 rates; ``roofline`` is for the dominant kernel (the Phase-1 flash kernel,
 bf16 MFMA), timed with HIP events on the stream it is launched on;
 ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample;
-``phase1.separate_rope`` times the same Phase 1 with the rotation of Q as a
-pass of its own.  Beside them: ``decode_cold`` (each step after a cache-flushing read),
+``phase1.separate_rope`` times the step's Phase 1 (the rotation of Q as a
+pass of its own) against the form that rotates Q inside the kernel.  Beside
+them: ``decode_cold`` (each step after a cache-flushing read),
 ``decode_graph`` (steps replayed from captured HIP graphs),
 ``phase2_query`` (the query partials against their roofline),
 ``hbm_stream`` (the streaming-read reference), ``phase1_variants``,
@@ -407,10 +408,11 @@ def decode_graph(st, w, ev, n):
 
 
 def phase1_separate_rope(st, dev, w, ev, reps=5):
-    """The same box, interleaved: the step's Phase-1 call (Q rotated inside
-    the kernel) against the rotation of Q as a pass of its own
-    (star_rope_apply) followed by star_phase1_blocklocal on the rotated Q.
-    Both give the same bits; the second kernel does attention only."""
+    """The same box, interleaved: Phase 1 with Q rotated inside the kernel
+    (star_phase1_rope) against the step's form, the rotation of Q as a pass
+    of its own (star_rope_apply) followed by star_phase1_blocklocal on the
+    rotated Q.  Both give the same bits; the second kernel does attention
+    only."""
     import numpy as np
     import torch
 
@@ -420,7 +422,8 @@ def phase1_separate_rope(st, dev, w, ev, reps=5):
     for _ in range(reps):
         e = [ev() for _ in range(4)]
         e[0].record()
-        st.phase1()
+        sa.phase1_rope(dev["q"], st.kc[:, :, :L], st.vc[:, :, :L], st.b, st.a, w.base,
+                       st.scale, out=st.o1, lse=st.lse1, sched=st.sched)
         e[1].record()
         sa.rope_apply(dev["q"], pos0=0, base=w.base, out=st.qr)
         e[2].record()
@@ -438,9 +441,9 @@ def phase1_separate_rope(st, dev, w, ev, reps=5):
             "blocklocal_tflops": fl / (med["blocklocal"] * 1e-3) / 1e12,
             "blocklocal_frac_of_peak": fl / (med["blocklocal"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "reps": reps,
-            "note": "medians of interleaved launches: star_phase1_rope (the step's call) "
-                    "against star_rope_apply on Q + star_phase1_blocklocal (same output "
-                    "bits; that kernel does attention only)"}
+            "note": "medians of interleaved launches: star_phase1_rope against the step's "
+                    "star_rope_apply on Q + star_phase1_blocklocal (same output bits; that "
+                    "kernel does attention only)"}
 
 
 def config_record(name, ev, rows_per_block=8, decode_steps=16):
@@ -739,6 +742,58 @@ def _short_kernel_name(name: str) -> str:
     return re.sub(r"^void ", "", short)
 
 
+def _trace_sequences(files) -> list:
+    """Launch-order figures of a step trace: each decode partials launch
+    with the merge launch that follows it, split into the cold samples (the
+    launch right before the decode launch is the cache-flushing reduction)
+    and the others (step passes and graph replays), each with its median
+    decode, merge and decode-start-to-merge-end times and the gap between
+    the two launches; and the Phase-2 query partials (flash kernel launches
+    below its largest grid) in launch order."""
+    import csv
+    import statistics
+    ev = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                try:
+                    grid = int(r.get("Grid_Size_X", 0))
+                    wg = int(r.get("Workgroup_Size_X", 1))
+                    ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                               _short_kernel_name(r.get("Kernel_Name", "?")), grid // max(wg, 1)))
+                except (KeyError, ValueError):
+                    continue
+    ev.sort()
+    out = []
+    pairs = {"cold": [], "other": []}
+    for i, (s0, e0, n, _) in enumerate(ev):
+        if not n.startswith("star::decode_kernel") or i + 1 >= len(ev):
+            continue
+        s1, e1, n1, _ = ev[i + 1]
+        if not n1.startswith("star::merge_kernel"):
+            continue
+        cold = i > 0 and ev[i - 1][2].startswith("at::native::reduce_kernel")
+        pairs["cold" if cold else "other"].append(((e0 - s0) / 1e3, (e1 - s1) / 1e3,
+                                                   (e1 - s0) / 1e3, (s1 - e0) / 1e3))
+    for k, label in (("cold", "decode steps right after the cache-flushing read"),
+                     ("other", "other decode steps (step passes, graph replays)")):
+        v = pairs[k]
+        if v:
+            med = [statistics.median(x[j] for x in v) for j in range(4)]
+            out.append(f"{label}: {len(v)} launches; median decode {med[0]:.2f} us, merge "
+                       f"{med[1]:.2f} us, decode start to merge end {med[2]:.2f} us, gap "
+                       f"between the launches {med[3]:.2f} us")
+    fl = [(s0, e0, g) for s0, e0, n, g in ev if n.startswith("star::flash2_kernel")]
+    if fl:
+        big = max(g for _, _, g in fl)
+        q = [(e0 - s0) / 1e3 for s0, e0, g in fl if g < big]
+        if q:
+            out.append("Phase-2 query partials (flash kernel below its largest grid), first "
+                       f"{min(len(q), 8)} in launch order: " + ", ".join(f"{x:.1f}" for x in q[:8])
+                       + " us")
+    return ([""] + out) if out else []
+
+
 def trace_summary(root: str) -> str:
     """Per-kernel count, mean, median and min duration (us) from the
     kernel_trace.csv files a ``rocprofv3 --kernel-trace --output-format csv``
@@ -768,6 +823,7 @@ def trace_summary(root: str) -> str:
     for (n, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{n:60s} {wg:10d} {len(v):6d} {statistics.mean(v):10.2f} "
                      f"{statistics.median(v):10.2f} {min(v):10.2f} {100 * sum(v) / tot:5.1f}%")
+    lines += _trace_sequences(files)
     stats = glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)
     if stats:
         lines += ["", "rocprofv3 --stats (one line per kernel name: every grid size together)",
@@ -781,6 +837,101 @@ def trace_summary(root: str) -> str:
                                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
                     except (KeyError, ValueError):
                         continue
+    return "\n".join(lines)
+
+
+def counter_summary(roots, calib_mib: int = 1024) -> str:
+    """Per-dispatch means of the counters in the counter_collection.csv
+    files that ``rocprofv3 --pmc ... --output-format csv`` runs wrote under
+    ``roots`` (one run per counter set), one line per (kernel, workgroup
+    count, counter); then, from the same numbers:
+      * byte counters scaled by the plain device copy of ``calib_mib`` MiB
+        the ``--copy-calib`` run issues first (__amd_rocclr_copyBuffer: its
+        bytes read and written are known), and the Phase-1 launch's
+        ``traffic_bytes_per_launch`` with the flash kernel's source hash (the
+        lines the benchmark's ``roofline.traffic`` reads);
+      * SQ ratios of the Phase-1 flash launch (the flash kernel's largest
+        grid) when its SQ counters are there."""
+    import csv
+    import glob
+    import statistics
+    agg = {}
+    for root in roots:
+        files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    try:
+                        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)))
+                        wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 1)))
+                        val = float(r["Counter_Value"])
+                        cname = r["Counter_Name"]
+                    except (KeyError, ValueError):
+                        continue
+                    key = (_short_kernel_name(r.get("Kernel_Name", "?"))[:60], grid // max(wg, 1))
+                    agg.setdefault(key, {}).setdefault(cname, []).append(val)
+    if not agg:
+        return f"no *counter_collection.csv under {roots}"
+    lines = [f"{'kernel':60s} {'workgroups':>10s} {'counter':28s} {'dispatches':>10s} "
+             f"{'mean':>14s} {'min':>14s} {'max':>14s}"]
+    for (n, wg), cs in sorted(agg.items()):
+        for c, v in sorted(cs.items()):
+            lines.append(f"{n:60s} {wg:10d} {c:28s} {len(v):10d} {statistics.mean(v):14.6g} "
+                         f"{min(v):14.6g} {max(v):14.6g}")
+    mean = {k: {c: statistics.mean(v) for c, v in cs.items()} for k, cs in agg.items()}
+    copy = next((cs for (n, _), cs in mean.items() if n.startswith("__amd_rocclr_copyBuffer")
+                 and cs.get("FETCH_SIZE", cs.get("WRITE_SIZE", 0)) > 0), None)
+    flash = [k for k in mean if k[0].startswith("star::flash2_kernel")]
+    p1 = max(flash, key=lambda k: k[1]) if flash else None
+    nbytes = calib_mib * (1 << 20)
+    if copy is not None:
+        lines += ["", f"calibration copy: {calib_mib} MiB read and written"]
+        scale = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in copy:
+                scale[c] = nbytes / (copy[c] * 1024.0)
+                lines.append(f"  {c} {copy[c]:.0f} KiB -> scale {scale[c]:.4f}")
+        lines.append("scaled bytes per dispatch (counter KiB x 1024 x scale):")
+        for (n, wg), cs in sorted(mean.items()):
+            parts = [f"{c} {cs[c] * 1024 * scale[c] / 1e9:.4f} GB" for c in scale if c in cs]
+            if parts:
+                lines.append(f"  {n:60s} {wg:10d}  " + ", ".join(parts))
+        if p1 is not None and all(c in mean[p1] for c in ("FETCH_SIZE", "WRITE_SIZE")) \
+                and len(scale) == 2:
+            tr = sum(mean[p1][c] * 1024 * scale[c] for c in scale)
+            src = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
+            lines += [f"Phase-1 launch ({p1[0]}, {p1[1]} workgroups): "
+                      f"read {mean[p1]['FETCH_SIZE'] * 1024 * scale['FETCH_SIZE'] / 1e9:.3f} GB, "
+                      f"written {mean[p1]['WRITE_SIZE'] * 1024 * scale['WRITE_SIZE'] / 1e9:.3f} GB",
+                      f"traffic_bytes_per_launch: {tr:.6e}",
+                      f"flash_src_sha256: {src}"]
+    if p1 is not None:
+        c = mean[p1]
+        need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA")
+        if all(x in c for x in need):
+            kc = c["GRBM_GUI_ACTIVE"] / 8.0
+            d = [("kernel cycles per XCD (GRBM_GUI_ACTIVE / 8)", kc),
+                 ("MFMA busy / SIMD cycles (1024 SIMDs)",
+                  c["SQ_VALU_MFMA_BUSY_CYCLES"] / (kc * 1024)),
+                 ("MFMA busy cycles / MFMA instruction",
+                  c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_INSTS_MFMA"])]
+            for label, num in (("VALU instructions / MFMA (incl. MFMA)", "SQ_INSTS_VALU"),
+                               ("exp2 (trans) / MFMA", "SQ_INSTS_VALU_TRANS_F32"),
+                               ("LDS instructions / MFMA", "SQ_INSTS_LDS"),
+                               ("SALU instructions / MFMA", "SQ_INSTS_SALU")):
+                if num in c:
+                    d.append((label, c[num] / c["SQ_INSTS_MFMA"]))
+            if all(x in c for x in ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY")):
+                wc = c["SQ_WAVE_CYCLES"]
+                d += [("wave cycles waiting (SQ_WAIT_ANY)", c["SQ_WAIT_ANY"] / wc),
+                      ("wave cycles ready, not issued",
+                       (wc - c["SQ_WAIT_ANY"] - c["SQ_ACTIVE_INST_ANY"]) / wc),
+                      ("wave cycles issuing", c["SQ_ACTIVE_INST_ANY"] / wc)]
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                d.append(("MFMA/VALU co-execution / MFMA busy",
+                          c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"]))
+            lines += ["", f"derived, Phase-1 launch ({p1[0]}, {p1[1]} workgroups):"]
+            lines += [f"  {label:42s} {v:.4g}" for label, v in d]
     return "\n".join(lines)
 
 
@@ -806,6 +957,9 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of this many MiB first "
                          "(reference kernel for rocprofv3 byte counters)")
+    ap.add_argument("--no-separate-rope", action="store_true",
+                    help="skip timing Phase 1 with Q rotated inside the kernel beside the "
+                         "step's form (keeps a kernel trace to the step's launches)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload records (timing + sampled parity)")
     ap.add_argument("--configs", default=None,
@@ -820,10 +974,17 @@ def main():
     ap.add_argument("--cpu-full-only", action="store_true",
                     help="with --cpu-full: time the oracle only (no GPU work) and print "
                          "one JSON line")
+    ap.add_argument("--counter-summary", nargs="+", default=None, metavar="DIR",
+                    help="print per-kernel counter means from the rocprofv3 --pmc csv runs "
+                         "under the DIRs (with byte scaling by the --copy-calib copy and the "
+                         "Phase-1 launch's ratios), then exit (no GPU)")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="print the per-kernel summary of a rocprofv3 --output-format csv "
                          "kernel trace found under DIR, then exit (no GPU)")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, args.copy_calib or 1024))
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return
@@ -929,9 +1090,9 @@ def main():
                      "traffic": pmc_traffic(),
                      "kernel": "flash2_kernel (Phase 1)"},
     }
-    if st.fuse_q_rope:
+    if w.rope and w.D == 128 and not args.phase1_only and not args.no_separate_rope:
         out["phase1"]["separate_rope"] = phase1_separate_rope(st, dev, w, ev)
-        progress("Phase 1 with the rotation of Q as its own pass done")
+        progress("Phase 1 with and without the rotation of Q inside the kernel done")
     if not args.phase1_only and w.T > 0:
         dec_ms = np.mean([r["dec"][0].elapsed_time(r["dec"][1]) for r in recs])
         byts = sum(decode_bytes(w, t) for t in range(w.T))

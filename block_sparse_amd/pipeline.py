@@ -59,7 +59,7 @@ class StarAttentionStep:
     def __init__(self, B, Hq, Hkv, D, L, b, Lq, T, anchor=None, rope=True,
                  base=500000.0, device="cuda", want_lse=True,
                  splits_query=None, splits_decode=None, fused_decode=True,
-                 fuse_q_rope=True, dynamic_schedule=True):
+                 fuse_q_rope=False, dynamic_schedule=True):
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
         self.L, self.b, self.Lq, self.T = L, b, Lq, T
         self.a = b if anchor is None else anchor
@@ -97,9 +97,12 @@ class StarAttentionStep:
         self.lp_d = torch.empty((nd, B, Hq, 1), dtype=torch.float32, device=dev)
         # rope + append + partials in one launch per token (star_decode_step)
         self.fused_decode = fused_decode
-        # Phase 1 rotates the context Q itself (star_phase1_rope): no separate
-        # pass over Q; the rotated copy self.qr is made only if a Phase-1
-        # variant needs it
+        # fuse_q_rope: Phase 1 rotates the context Q itself
+        # (star_phase1_rope) instead of a RoPE pass over Q into self.qr
+        # before star_phase1_blocklocal.  Both give the same bits; measured
+        # at 8B-128K on three boxes, the separate pass plus the attention-only
+        # kernel took the same or less time (by 0.2-1.6%), so it is the
+        # default.
         self.fuse_q_rope = bool(fuse_q_rope and rope and D == 128)
         # Phase-1 work items from per-XCD queues (the calls of one step run
         # in order on one stream, so one workspace serves them all)

@@ -2,7 +2,10 @@
 call sequence the benchmark times (block_sparse_amd.pipeline).
 
 Tiny is compared on every output element, in both its fp32 and bf16 forms.
-The Llama-shaped workloads are compared for every (batch, query head):
+The Llama-shaped workloads are compared for every (batch, query head), on
+the call sequence the benchmark times (Q rotated in a pass of its own before
+Phase 1), and Phase 1 with Q rotated inside the kernel is checked bit for bit
+against it at full size:
   * the rotated K cache (context, query and decode rows): bit for bit
     against the oracle's exact rotation rounded once to bf16;
   * Phase 1: llama8b-16k on every row; the larger ones on the first two and
@@ -97,6 +100,17 @@ def test_llama_workload(name):
     st.load_context(to_dev(x["v"]))
     st.run(dev["q"], dev["k"], dev["qq"], dev["kq"], dev["vq"], dev["qd"], dev["kd"], dev["vd"])
     torch.cuda.synchronize()
+    # the step rotates Q in a pass of its own; the Phase-1 form that rotates
+    # Q inside the kernel gives the same bits at full size
+    log(f"{name}: Phase 1 with the rotation of Q inside the kernel")
+    of = torch.empty_like(st.o1)
+    lf = torch.empty_like(st.lse1)
+    sa.phase1_rope(dev["q"], st.kc[:, :, :w.L], st.vc[:, :, :w.L], w.b, w.a, w.base, scale,
+                   out=of, lse=lf, sched=st.sched)
+    torch.cuda.synchronize()
+    assert torch.equal(of.view(torch.int16), st.o1.view(torch.int16)), "fused-RoPE O differs"
+    assert torch.equal(lf.view(torch.int32), st.lse1.view(torch.int32)), "fused-RoPE lse differs"
+    del of, lf
     # properties over every head at full size
     assert bool(torch.isfinite(st.o1).all()), "non-finite Phase-1 output"
     assert bool(torch.isfinite(st.lse1).all()), "non-finite Phase-1 lse"
