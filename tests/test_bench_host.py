@@ -139,3 +139,106 @@ def test_oracle_flops_follow_the_oracles_key_sets():
         per_head += 4 * w.D * mask.shape[0] * mask.shape[1]
     assert bench.oracle_flops(w) == per_head * w.Hq * w.B
     assert bench.oracle_flops(w, 2) < bench.oracle_flops(w)
+
+
+def _trace_row(i, name, start, end, wg=256, block=512):
+    return (f'KERNEL_DISPATCH,1,1,1,1,{i},1,"{name}",{i},{start},{end},0,0,{block},1,1,'
+            f'{block * wg},1,1\n')
+
+
+def test_trace_sequences_cold_and_query(tmp_path):
+    """Launch-order figures: a decode launch right after the flushing
+    reduction is a cold sample, its merge follows it; flash launches below the
+    largest grid are the query partials, in launch order."""
+    bench = load_bench()
+    hdr = ("Kind,Agent_Id,Queue_Id,Stream_Id,Thread_Id,Dispatch_Id,Kernel_Id,Kernel_Name,"
+           "Correlation_Id,Start_Timestamp,End_Timestamp,Private_Segment_Size,"
+           "Group_Segment_Size,Workgroup_Size_X,Workgroup_Size_Y,Workgroup_Size_Z,"
+           "Grid_Size_X,Grid_Size_Y,Grid_Size_Z\n")
+    dec = "void star::(anonymous namespace)::decode_kernel<128, __bf16, true>(star::DecodeParams)"
+    mrg = "void star::(anonymous namespace)::merge_kernel<128>(star::MergeParams)"
+    red = "void at::native::reduce_kernel<512, 1>(int)"
+    fl = "star::(anonymous namespace)::flash2_kernel(star::FlashParams)"
+    rows, t, i = [], 0, 0
+
+    def add(name, dur_ns, wg=256, gap=0):
+        nonlocal t, i
+        rows.append(_trace_row(i, name, t + gap, t + gap + dur_ns, wg))
+        t += gap + dur_ns
+        i += 1
+    add(fl, 40_000_000, wg=18440)
+    add(fl, 140_000, gap=5000)
+    add(fl, 150_000, gap=5000)
+    for cold in (True, False, True, False):
+        if cold:
+            add(red, 270_000, wg=1, gap=3000)
+        add(dec, 88_000 if cold else 86_000, gap=2000)
+        add(mrg, 4_000, wg=32, gap=500)
+    (tmp_path / "run_kernel_trace.csv").write_text(hdr + "".join(rows))
+    out = bench.trace_summary(str(tmp_path))
+    cold = next(l for l in out.splitlines() if l.startswith("decode steps right after"))
+    warm = next(l for l in out.splitlines() if l.startswith("other decode steps"))
+    assert "2 launches; median decode 88.00 us, merge 4.00 us" in cold
+    assert "decode start to merge end 92.50 us, gap between the launches 0.50 us" in cold
+    assert "2 launches; median decode 86.00 us" in warm
+    q = next(l for l in out.splitlines() if l.startswith("Phase-2 query partials"))
+    assert q.endswith("first 2 in launch order: 140.0, 150.0 us")
+
+
+def _counter_rows(name, grid_wg, counters, start=0):
+    out = []
+    for c, v in counters.items():
+        out.append(f'{start},{start},"Agent 1",1,1,1,{grid_wg * 512},1,"{name}",512,0,0,128,0,96,'
+                   f'"{c}",{v},{start},{start + 10}\n')
+    return out
+
+
+def test_counter_summary_scales_bytes_by_the_copy(tmp_path):
+    """Byte counters are scaled by the plain copy of known size (fetch read
+    at half: scale 2, writes at full: scale 1), and the Phase-1 launch's
+    traffic line carries the flash kernel's source hash, as the benchmark's
+    roofline reads it."""
+    import hashlib
+    bench = load_bench()
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
+           '"Grid_Size","Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size",'
+           '"Scratch_Size","VGPR_Count","Accum_VGPR_Count","SGPR_Count","Counter_Name",'
+           '"Counter_Value","Start_Timestamp","End_Timestamp"\n')
+    fl = "star::(anonymous namespace)::flash2_kernel(star::FlashParams)"
+    for sub, c, copy_v, fl_v in (("f", "FETCH_SIZE", 524288, 1_000_000),
+                                 ("w", "WRITE_SIZE", 1048576, 500_000)):
+        d = tmp_path / sub
+        d.mkdir()
+        rows = (_counter_rows("__amd_rocclr_copyBuffer", 1, {c: copy_v})
+                + _counter_rows(fl, 256, {c: 7}, 5) + _counter_rows(fl, 18440, {c: fl_v}, 9))
+        (d / "run_counter_collection.csv").write_text(hdr + "".join(rows))
+    out = bench.counter_summary([str(tmp_path / "f"), str(tmp_path / "w")], 1024)
+    want = (1_000_000 * 2.0 + 500_000 * 1.0) * 1024
+    line = next(l for l in out.splitlines() if l.startswith("traffic_bytes_per_launch:"))
+    assert abs(float(line.split(":")[1]) - want) / want < 1e-6
+    src = hashlib.sha256(open(os.path.join(ROOT, "block_sparse_amd", "csrc", "flash2.hip"),
+                              "rb").read()).hexdigest()
+    assert f"flash_src_sha256: {src}" in out
+
+
+def test_counter_summary_sq_ratios(tmp_path):
+    """The Phase-1 launch's SQ ratios: MFMA busy over the SIMD cycles of the
+    launch (GRBM_GUI_ACTIVE summed over 8 XCDs, 1024 SIMDs) and per-MFMA
+    instruction counts."""
+    bench = load_bench()
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
+           '"Grid_Size","Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size",'
+           '"Scratch_Size","VGPR_Count","Accum_VGPR_Count","SGPR_Count","Counter_Name",'
+           '"Counter_Value","Start_Timestamp","End_Timestamp"\n')
+    fl = "star::(anonymous namespace)::flash2_kernel(star::FlashParams)"
+    c = {"GRBM_GUI_ACTIVE": 8 * 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1000 * 1024,
+         "SQ_INSTS_MFMA": 500, "SQ_INSTS_VALU": 2000, "SQ_WAVE_CYCLES": 100,
+         "SQ_WAIT_ANY": 30, "SQ_ACTIVE_INST_ANY": 45}
+    (tmp_path / "run_counter_collection.csv").write_text(hdr + "".join(_counter_rows(fl, 18440, c)))
+    out = bench.counter_summary([str(tmp_path)])
+    val = {l.rsplit(None, 1)[0].strip(): float(l.split()[-1]) for l in out.splitlines()
+           if l.startswith("  ") and l.split()[-1][0].isdigit()}
+    assert val["MFMA busy / SIMD cycles (1024 SIMDs)"] == pytest.approx(0.5)
+    assert val["VALU instructions / MFMA (incl. MFMA)"] == pytest.approx(4.0)
+    assert val["wave cycles waiting (SQ_WAIT_ANY)"] == pytest.approx(0.30)
+    assert val["wave cycles ready, not issued"] == pytest.approx(0.25)
