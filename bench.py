@@ -487,10 +487,16 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
                            base=w.base)
     st.load_context(v)
     st.rope_context(q, k)
-    st.phase1()
-    torch.cuda.synchronize()
-    # launches back to back (a short kernel right after an idle pause runs
-    # before the clock has ramped up): the median of 5, 2 at the 1M shape
+    # warm-up: Phase 1 back to back for at least 0.2 s (a short kernel right
+    # after the host-side work of the previous record would otherwise run
+    # before the clock has ramped up), then the median of 5 launches, 2 at
+    # the 1M shape
+    t_w = time.perf_counter()
+    while True:
+        st.phase1()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_w >= 0.2:
+            break
     e = [(ev(), ev()) for _ in range(2 if w.L >= (1 << 20) else 5)]
     for e0, e1 in e:
         e0.record()
