@@ -862,6 +862,7 @@ def counter_summary(roots, calib_mib: int = 1024) -> str:
     import glob
     import statistics
     agg = {}
+    dur = {}
     for root in roots:
         files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
         for f in files:
@@ -876,6 +877,11 @@ def counter_summary(roots, calib_mib: int = 1024) -> str:
                         continue
                     key = (_short_kernel_name(r.get("Kernel_Name", "?"))[:60], grid // max(wg, 1))
                     agg.setdefault(key, {}).setdefault(cname, []).append(val)
+                    try:
+                        dur[(key, r["Dispatch_Id"], root)] = (
+                            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                    except (KeyError, ValueError):
+                        pass
     if not agg:
         return f"no *counter_collection.csv under {roots}"
     lines = [f"{'kernel':60s} {'workgroups':>10s} {'counter':28s} {'dispatches':>10s} "
@@ -916,7 +922,13 @@ def counter_summary(roots, calib_mib: int = 1024) -> str:
         need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA")
         if all(x in c for x in need):
             kc = c["GRBM_GUI_ACTIVE"] / 8.0
-            d = [("kernel cycles per XCD (GRBM_GUI_ACTIVE / 8)", kc),
+            d = [("kernel cycles per XCD (GRBM_GUI_ACTIVE / 8)", kc)]
+            ns = [v for (k, _, _), v in dur.items() if k == p1]
+            if ns:
+                d += [("launch duration in the counter runs (ms)", statistics.mean(ns) / 1e6),
+                      ("clock (those cycles / that duration, GHz)",
+                       kc / statistics.mean(ns))]
+            d += [
                  ("MFMA busy / SIMD cycles (1024 SIMDs)",
                   c["SQ_VALU_MFMA_BUSY_CYCLES"] / (kc * 1024)),
                  ("MFMA busy cycles / MFMA instruction",
