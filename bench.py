@@ -319,7 +319,8 @@ def phase2_query(st, w, ev, in_step_ms, reps=20):
     min(MFMA peak, arithmetic intensity x HBM peak).
 
     ``in_step_ms``: the partials call's duration inside each timed step
-    (events recorded right around it), the reported figure.  The call runs
+    (events recorded right around it), the reported figure (None: report
+    the sustained rate).  The call runs
     once per step, right after Phase 1; timed back to back instead, the
     kernel's clock moves with the chip's power management (a trace at
     8B-128K shows ~135 us for the first dozen launches, then 160-200 us), so
@@ -343,7 +344,7 @@ def phase2_query(st, w, ev, in_step_ms, reps=20):
 
     timed(1)
     sustained = [timed(reps) for _ in range(3)]
-    ms = float(np.median(in_step_ms))
+    ms = float(np.median(in_step_ms if in_step_ms else sustained))
     fl, by = query_flops(w), query_bytes(w)
     tflops = fl / (ms * 1e-3) / 1e12
     gbps = by / (ms * 1e-3) / 1e9
@@ -352,7 +353,7 @@ def phase2_query(st, w, ev, in_step_ms, reps=20):
     sus = float(np.median(sustained))
     return {"us": ms * 1e3, "tflops": tflops, "gbps": gbps, "flops": fl, "bytes": by,
             "arith_intensity": ai, "roofline_tflops": roof, "frac_of_roofline": tflops / roof,
-            "samples": len(in_step_ms),
+            "samples": len(in_step_ms) if in_step_ms else 0,
             "sustained_us": sus * 1e3,
             "sustained_frac_of_roofline": fl / (sus * 1e-3) / 1e12 / roof,
             "splits": st.sq,
@@ -510,6 +511,10 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
            "phase1_frac_of_peak": fl / (p1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "context_tokens_per_s": w.B * w.L / (p1_ms * 1e-3)}
     st.query(qq, kq, vq)
+    if w.Lq > 0:
+        pq = phase2_query(st, w, ev, None, reps=5)
+        rec.update({"query_us": pq["us"], "query_frac_of_roofline": pq["frac_of_roofline"],
+                    "query_splits": pq["splits"]})
     if n_dec:
         e0, e1 = ev(), ev()
         e0.record()

@@ -43,7 +43,9 @@
 // One workgroup = 8 waves, one 32-row column block each; 64-key tiles in
 // three LDS buffers (one tile computing, one landing, one free); two waves
 // share a SIMD, so one's LDS reads, barrier waits and exps run under the
-// other's MFMAs.
+// other's MFMAs.  Phase-2 query items with at most 4 column blocks run a
+// 4-wave instance with 32-key tiles instead: two of its workgroups share a
+// CU, so the second wave of a SIMD comes from the other workgroup.
 #include "common.h"
 #include "internal.h"
 #include "flash_items.h"
@@ -55,13 +57,9 @@ namespace star {
 namespace {
 
 constexpr int D = 128;
-constexpr int NW = 8;
-constexpr int KT = 64;
 constexpr int ROWB = D * 2;                 // bytes per K/V row
-constexpr int TILE = KT * ROWB;             // 16 KiB
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kRescaleP = 256.0f;          // 2^kRescaleLog2
-constexpr int NBUF = 3;                     // LDS tile buffers
 
 // s_waitcnt vmcnt(4): all but this wave's last 4 vector-memory ops done
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
@@ -191,7 +189,18 @@ __device__ __forceinline__ void rope_q_pass(bf16x8* qf, int j0, int FPP, int r, 
   }
 }
 
-__global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
+// NW waves, tiles of KT = 32 SUB keys (SUB 32-key sub-tiles each).  The
+// instance <8, 2> serves Phase 1 and the Phase-2 query; <4, 1> serves query
+// items whose rows fill at most 4 column blocks: with 48 KiB of LDS two of
+// its workgroups share a CU, so no wave computes columns without rows.
+template <int NW, int SUB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void flash2_kernel(const FlashParams p) {
+  constexpr int KT = 32 * SUB;
+  constexpr int TILE = KT * ROWB;             // 16 KiB (SUB = 2), 8 KiB (SUB = 1)
+  constexpr int NBUF = 3;                     // LDS tile buffers
+  constexpr int CYC = NBUF * SUB;             // sub-tiles per cycle of the buffer ring
+  static_assert(NW * 8 == KT && (SUB == 1 || SUB == 2), "each wave loads 8 rows of a tile");
   // tile buffer b: K rows at smK + b TILE, V rows at smV + b TILE
   __shared__ __attribute__((aligned(1024))) uint8_t smK[NBUF * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t smV[NBUF * TILE];
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
 
   const int nt0 = (int)((it.ra1 - it.ra0 + KT - 1) / KT);
   const int nt = nt0 + (int)((it.rb1 - it.rb0 + KT - 1) / KT);
-  const int nsub = 2 * nt;                        // 32-key sub-tiles
+  const int nsub = SUB * nt;                      // 32-key sub-tiles
 
   // Tiles are loaded in order, range A's then range B's.  The loader keeps
   // the next tile's K and V row pointers (advanced by one 64-bit add per
@@ -369,9 +378,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   float msub = 0.f;          // m2 where finite, else 0 (the exp2 shift)
   const float c2 = p.scale_log2;
 
-  // Sub-tile j (32 keys) lives in LDS buffer (j / 2) % 3, rows 32 (j % 2) ..
-  // The loop below is unrolled over the 6 sub-tiles of one buffer cycle so
-  // that every LDS address is a per-lane register plus an immediate.
+  // Sub-tile j (32 keys) lives in LDS buffer (j / SUB) % 3, rows 32 (j % SUB) ..
+  // The loop below is unrolled over the 3 SUB sub-tiles of one buffer cycle
+  // so that every LDS address is a per-lane register plus an immediate.
   auto qk = [&](auto boff) -> f32x16 {
     constexpr int OFF = decltype(boff)::value;
     f32x16 s;
@@ -385,8 +394,9 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // first key of sub-tile j, relative to the start of its key range, and
   // the range it belongs to
   auto sub_key = [&](int j) -> int64_t {
-    const int t = j >> 1;
-    return (t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0)) + 32 * (j & 1);
+    const int t = SUB == 2 ? j >> 1 : j;
+    return (t < nt0 ? it.ra0 + (int64_t)KT * t : it.rb0 + (int64_t)KT * (t - nt0)) +
+           32 * (j & (SUB - 1));
   };
   // keys of sub-tile j past the range end or (range B only) after the row's
   // position -> -inf
@@ -397,11 +407,11 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   int jmB;
   {
     const int64_t xb = wave_min - 31 - it.rb0;
-    jmB = 2 * nt0 + (int)min((it.rb1 - it.rb0) >> 5, xb < 0 ? (int64_t)0 : (xb >> 5) + 1);
+    jmB = SUB * nt0 + (int)min((it.rb1 - it.rb0) >> 5, xb < 0 ? (int64_t)0 : (xb >> 5) + 1);
   }
-  auto mask_needed = [&](int j) -> bool { return j >= (j < 2 * nt0 ? jmA : jmB); };
+  auto mask_needed = [&](int j) -> bool { return j >= (j < SUB * nt0 ? jmA : jmB); };
   auto mask = [&](int j, f32x16& s) {
-    const bool A = j < 2 * nt0;
+    const bool A = j < SUB * nt0;
     const int64_t ks = sub_key(j);
     const int64_t rend = A ? it.ra1 : it.rb1;
     const int lim_end = (int)min(rend - ks, (int64_t)32);
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
   // an entry is wave-uniform for NR >= 64 and takes one of two values for
   // NR = 32, so its loads are scalar ones and the compiler's wait for them
   // does not also wait for the tile DMAs in flight.
-  if (p.q_rope) {
+  if constexpr (SUB == 2) if (p.q_rope) {
     typedef double f64x2 __attribute__((ext_vector_type(2)));
     const int NR = 32 * p.npg;
     const int FPP = 2048 / NR;
@@ -502,22 +512,22 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     if (mask_needed(0)) mask(0, s);
   }
 
-  // one pipeline step: sub-tile j = 6c + JJ (buffer JJ / 2, half JJ % 2).
-  // On entry s = S_j, masked.
+  // one pipeline step: sub-tile j = CYC c + JJ (buffer JJ / SUB, sub-tile
+  // JJ % SUB of it).  On entry s = S_j, masked.
   auto step = [&](auto jjc, int j) {
     constexpr int JJ = decltype(jjc)::value;
-    constexpr int CUR = (JJ >> 1) * TILE + (JJ & 1) * 32 * ROWB;         // this sub-tile
-    constexpr int JN = (JJ + 1) % 6;
-    constexpr int NXT = (JN >> 1) * TILE + (JN & 1) * 32 * ROWB;         // the next one
+    constexpr int CUR = (JJ / SUB) * TILE + (JJ % SUB) * 32 * ROWB;       // this sub-tile
+    constexpr int JN = (JJ + 1) % CYC;
+    constexpr int NXT = (JN / SUB) * TILE + (JN % SUB) * 32 * ROWB;       // the next one
     const bool more = j + 1 < nsub;
-    if constexpr ((JJ & 1) == 1) {
+    if constexpr (JJ % SUB == SUB - 1) {
       // the next sub-tile starts a new tile: make it resident, then put the
       // tile after it in flight (its buffer was last read two tiles ago)
       if (more) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const int tn = (j >> 1) + 2;
-        if (tn < nt) load_next(((JJ >> 1) + 2) % NBUF);
+        const int tn = j / SUB + 2;
+        if (tn < nt) load_next((JJ / SUB + 2) % NBUF);
       }
     }
     // P_j with the current shift, issued together with the QK MFMAs of
@@ -566,24 +576,28 @@ __global__ __launch_bounds__(NW * 64) void flash2_kernel(const FlashParams p) {
     s = sn;
   };
 
-  // whole 6-sub-tile cycles without an exit in the middle (an exit there
+  // whole CYC-sub-tile cycles without an exit in the middle (an exit there
   // makes the compiler materialise the dead loop state of the exit path in
   // every step, stalling on the last MFMA's result), then the remainder
-  const int ncyc = nsub / 6, rem = nsub - 6 * ncyc;
+  const int ncyc = nsub / CYC, rem = nsub - CYC * ncyc;
   int j = 0;
-  for (int c = 0; c < ncyc; ++c, j += 6) {
+  for (int c = 0; c < ncyc; ++c, j += CYC) {
     step(std::integral_constant<int, 0>{}, j);
     step(std::integral_constant<int, 1>{}, j + 1);
     step(std::integral_constant<int, 2>{}, j + 2);
-    step(std::integral_constant<int, 3>{}, j + 3);
-    step(std::integral_constant<int, 4>{}, j + 4);
-    step(std::integral_constant<int, 5>{}, j + 5);
+    if constexpr (CYC == 6) {
+      step(std::integral_constant<int, 3 % CYC>{}, j + 3);
+      step(std::integral_constant<int, 4 % CYC>{}, j + 4);
+      step(std::integral_constant<int, 5 % CYC>{}, j + 5);
+    }
   }
   if (rem > 0) step(std::integral_constant<int, 0>{}, j);
   if (rem > 1) step(std::integral_constant<int, 1>{}, j + 1);
-  if (rem > 2) step(std::integral_constant<int, 2>{}, j + 2);
-  if (rem > 3) step(std::integral_constant<int, 3>{}, j + 3);
-  if (rem > 4) step(std::integral_constant<int, 4>{}, j + 4);
+  if constexpr (CYC == 6) {
+    if (rem > 2) step(std::integral_constant<int, 2>{}, j + 2);
+    if (rem > 3) step(std::integral_constant<int, 3 % CYC>{}, j + 3);
+    if (rem > 4) step(std::integral_constant<int, 4 % CYC>{}, j + 4);
+  }
 
   // ---- epilogue
   const float lt = lsum + __shfl_xor(lsum, 32);
@@ -631,6 +645,10 @@ bool flash2_supported(const FlashParams& p) {
 }
 
 hipError_t launch_flash2(FlashParams& p, hipStream_t stream) {
+  // Phase-2 query items of at most 4 column blocks (g <= 4 heads x their
+  // rows): the 4-wave instance, two workgroups per CU
+  const bool small = p.mode == 1 && !p.q_rope && p.g <= 4 && (int64_t)p.g * p.q_rows <= 128;
+  const int NW = small ? 4 : 8;
   if (!flash_geometry(p, NW)) return hipErrorInvalidValue;
   if (p.total_items == 0) return hipSuccess;
   int grid = p.total_items;
@@ -642,7 +660,10 @@ hipError_t launch_flash2(FlashParams& p, hipStream_t stream) {
     grid += spare;
     hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.sched);
   }
-  hipLaunchKernelGGL(flash2_kernel, dim3(grid), dim3(NW * 64), 0, stream, p);
+  if (small)
+    hipLaunchKernelGGL((flash2_kernel<4, 1>), dim3(grid), dim3(4 * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((flash2_kernel<8, 2>), dim3(grid), dim3(8 * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -83,10 +83,14 @@ class StarAttentionStep:
         self.P = -(-L // b)
         part_len = min(b, L)
         # query chunks: one workgroup per CU (256 at 8B-128K) -- measured
-        # 164 us against 190 us for two rounds of half-length chunks
+        # 164 us against 190 us for two rounds of half-length chunks.  With
+        # g <= 4 heads of at most 128 rows together (D = 128) the query runs
+        # the 4-wave flash instance, two workgroups per CU: 512 of them.
         g = Hq // Hkv
         rows = g * max(Lq, 1)
-        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len, 256, 512,
+        two_per_cu = D == 128 and g <= 4 and 16 < rows <= 128
+        self.sq = splits_query or choose_splits(B, Hkv, self.P, part_len,
+                                                512 if two_per_cu else 256, 512,
                                                 1 if rows <= 16 else math.ceil(rows / 256))
         self.sd = splits_decode or choose_splits(B, Hkv, self.P, part_len, 256, 512)
         nq = self.P * self.sq

@@ -207,6 +207,14 @@ P2_CASES = [
     (2, 8, 2, 128, 777, 1, 200, 4, False),   # decode path, fp32 inputs (rounded at load)
     (1, 4, 1, 64, 300, 1, 100, 8, False),    # decode path, D = 64, fp32 inputs
     (1, 16, 2, 128, 500, 16, 128, 2, False),  # flash path (g*Lq = 128), D = 128, fp32 inputs
+    # 4-wave flash instance (g <= 4, g*Lq <= 128, bf16, D = 128)
+    (1, 32, 8, 128, 1000, 32, 300, 2),  # g = 4, 128 rows, ragged chunks (5 tiles + tail)
+    (1, 8, 2, 128, 384, 32, 192, 2),    # chunks of 96 keys: whole 3-tile cycles
+    (1, 8, 2, 128, 512, 32, 256, 2),    # chunks of 128 keys: one tile past a cycle
+    (1, 8, 4, 128, 777, 20, 200, 3),    # g = 2, 40 rows: two column blocks per head
+    (2, 12, 4, 128, 901, 9, 256, 5),    # g = 3: the fourth wave has no column block
+    (1, 4, 4, 128, 640, 40, 160, 2),    # g = 1, 40 rows: waves 2, 3 idle
+    (1, 8, 2, 128, 500, 33, 128, 2),    # g*Lq = 132: just past it, the 8-wave instance
 ]
 
 
