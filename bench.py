@@ -738,9 +738,26 @@ def _short_kernel_name(name: str) -> str:
             parts.append(name[j:j + n])
             i = j + n
         targs = ""
-        if name[i:i + 1] == "I" and "E" in name[i:]:
-            code = name[i + 1:name.index("E", i)]
-            targs = "<" + {"DF16b": "__bf16", "f": "float", "d": "double"}.get(code, code) + ">"
+        if name[i:i + 1] == "I":
+            # template arguments: types (f, d, i, DF16b) and literals
+            # (L <type> <value> E: Li8E, Lb1E), up to the list's closing E
+            args, i = [], i + 1
+            types = {"DF16b": "__bf16", "f": "float", "d": "double", "i": "int", "b": "bool"}
+            while i < len(name) and name[i] != "E":
+                if name[i] == "L":
+                    j = name.index("E", i)
+                    lit = name[i + 1:j]
+                    t = "b" if lit[:1] == "b" else lit[:1]
+                    v = lit[1:]
+                    args.append({"0": "false", "1": "true"}[v] if t == "b" else v.replace("n", "-"))
+                    i = j + 1
+                    continue
+                code = next((c for c in types if name.startswith(c, i)), None)
+                if code is None:
+                    break
+                args.append(types[code])
+                i += len(code)
+            targs = "<" + ", ".join(args) + ">" if args else ""
         return "::".join(x for x in parts if not x.startswith("_GLOBAL__N")) + targs
     short = name.replace("(anonymous namespace)::", "")
     if short.endswith(")"):                       # drop the argument list

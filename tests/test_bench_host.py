@@ -106,6 +106,12 @@ def test_short_kernel_names():
              "long, unsigned int*)") == "star::stream_read_kernel"
     assert f("void star::(anonymous namespace)::merge_kernel<128>(star::MergeParams)") == \
         "star::merge_kernel<128>"
+    assert f("_ZN4star12_GLOBAL__N_113flash2_kernelILi4ELi1EEEvNS_11FlashParamsE") == \
+        "star::flash2_kernel<4, 1>"
+    assert f("_ZN4star12_GLOBAL__N_113decode_kernelILi128EDF16bLb1EEEvNS_12DecodeParamsE") == \
+        "star::decode_kernel<128, __bf16, true>"
+    assert f("void star::(anonymous namespace)::flash2_kernel<8, 2>(star::FlashParams)") == \
+        "star::flash2_kernel<8, 2>"
 
 
 def test_pages_host_flops():
