@@ -913,8 +913,11 @@ def counter_summary(roots, calib_mib: int = 1024) -> str:
             lines.append(f"{n:60s} {wg:10d} {c:28s} {len(v):10d} {statistics.mean(v):14.6g} "
                          f"{min(v):14.6g} {max(v):14.6g}")
     mean = {k: {c: statistics.mean(v) for c, v in cs.items()} for k, cs in agg.items()}
-    copy = next((cs for (n, _), cs in mean.items() if n.startswith("__amd_rocclr_copyBuffer")
-                 and cs.get("FETCH_SIZE", cs.get("WRITE_SIZE", 0)) > 0), None)
+    # the calibration copy: the largest copyBuffer dispatch (a step also
+    # issues small host-to-device copies through the same kernel)
+    copy = max((cs for (n, _), cs in mean.items() if n.startswith("__amd_rocclr_copyBuffer")
+                and cs.get("FETCH_SIZE", cs.get("WRITE_SIZE", 0)) > 0),
+               key=lambda cs: cs.get("FETCH_SIZE", 0) + cs.get("WRITE_SIZE", 0), default=None)
     flash = [k for k in mean if k[0].startswith("star::flash2_kernel")]
     p1 = max(flash, key=lambda k: k[1]) if flash else None
     nbytes = calib_mib * (1 << 20)

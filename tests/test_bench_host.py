@@ -203,7 +203,8 @@ def test_counter_summary_scales_bytes_by_the_copy(tmp_path):
     """Byte counters are scaled by the plain copy of known size (fetch read
     at half: scale 2, writes at full: scale 1), and the Phase-1 launch's
     traffic line carries the flash kernel's source hash, as the benchmark's
-    roofline reads it."""
+    roofline reads it.  A smaller copyBuffer dispatch (a host copy of the
+    step) is not taken for the calibration."""
     import hashlib
     bench = load_bench()
     hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
@@ -215,7 +216,10 @@ def test_counter_summary_scales_bytes_by_the_copy(tmp_path):
                                  ("w", "WRITE_SIZE", 1048576, 500_000)):
         d = tmp_path / sub
         d.mkdir()
-        rows = (_counter_rows("__amd_rocclr_copyBuffer", 1, {c: copy_v})
+        # a small host copy through the same kernel comes first: the
+        # calibration is the large one
+        rows = (_counter_rows("__amd_rocclr_copyBuffer", 1, {c: 3}, 1)
+                + _counter_rows("__amd_rocclr_copyBuffer", 256, {c: copy_v}, 2)
                 + _counter_rows(fl, 256, {c: 7}, 5) + _counter_rows(fl, 18440, {c: fl_v}, 9))
         (d / "run_counter_collection.csv").write_text(hdr + "".join(rows))
     out = bench.counter_summary([str(tmp_path / "f"), str(tmp_path / "w")], 1024)

@@ -87,6 +87,8 @@ P2_POISON_CASES = [
     # B, Hq, Hkv, D, L, Lq, b, splits, bf16   (path)
     (1, 32, 8, 128, 1000, 64, 300, 2, True),      # flash2 (D = 128 bf16), ragged last tile
     (1, 16, 4, 128, 777, 33, 200, 3, True),       # flash2, chunk ends at 32 mod 64
+    (1, 32, 8, 128, 1000, 32, 300, 2, True),      # flash2 4-wave (g * Lq = 128), ragged tile
+    (1, 8, 4, 128, 777, 20, 200, 3, True),        # flash2 4-wave, g = 2
     (1, 8, 2, 64, 700, 40, 256, 2, True),         # flash.hip (D = 64)
     (1, 16, 2, 128, 500, 16, 128, 2, False),      # flash.hip (fp32 inputs)
     (2, 8, 2, 128, 777, 1, 200, 4, True),         # decode kernel (g * Lq = 4)
@@ -208,9 +210,11 @@ def test_phase1_prefix_ignores_rows_outside_the_ranges(D, bf16):
 # ---------------------------------------------------------------------------
 # canaries: nothing outside an output is written
 # ---------------------------------------------------------------------------
-def test_outputs_keep_their_canaries():
-    B, Hq, Hkv, D, L, b, Lq = 1, 16, 4, 128, 700, 256, 40
-    print("canaries", flush=True)
+@pytest.mark.parametrize("Lq", [40, 24], ids=["8-wave", "4-wave"])
+def test_outputs_keep_their_canaries(Lq):
+    """(g * Lq = 160 runs the 8-wave query instance, 96 the 4-wave one.)"""
+    B, Hq, Hkv, D, L, b = 1, 16, 4, 128, 700, 256
+    print(f"canaries Lq={Lq}", flush=True)
     q, k, v = (to_dev(rand_tensor(64, t, B, H, L, D)) for t, H in ((0, Hq), (1, Hkv), (2, Hkv)))
     M = 64
     # Phase-1 O through a strided view laid out like the attention layer's
