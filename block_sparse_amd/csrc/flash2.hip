@@ -31,6 +31,10 @@
 //    results), O rescaled and P_j recomputed.  Per 32 keys a wave issues
 //    16 MFMAs and 57 other VALU instructions (16 FMA, 16 exp, 16 adds,
 //    8 packs, 1 compare).
+//  * each step's softmax and next QK MFMAs run at a raised wave priority
+//    (s_setprio), the PV MFMAs at the normal one: the two waves of a SIMD
+//    then tend to alternate, one's VALU work beside the other's MFMAs
+//    (1.8-2.7% faster at 8B-128K than without, same box).
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
@@ -532,10 +536,14 @@ void flash2_kernel(const FlashParams p) {
     }
     // P_j with the current shift, issued together with the QK MFMAs of
     // S_{j+1} (after the last sub-tile S_{j+1} is unused: its slot may hold
-    // stale data)
+    // stale data).  The wave runs this part at a raised issue priority, so
+    // of the two waves of a SIMD the one in its softmax goes ahead while the
+    // other is in its PV MFMAs: the two fall into alternating phases.
     bf16x8 pf[2];
+    __builtin_amdgcn_s_setprio(1);
     float ls = softmax_p(s, pf);
     f32x16 sn = qk(std::integral_constant<int, NXT>{});
+    __builtin_amdgcn_s_setprio(0);
     // Lazy rescale, tested after the fact: a column whose scores exceed
     // its shift by more than 8 (log2 units) has a P above 2^8, so its lane
     // sum exceeds 2^8.  Only a wave where some lane's sum exceeds plim
