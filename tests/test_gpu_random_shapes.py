@@ -100,7 +100,28 @@ def _p2_cases(n, seed):
     return out
 
 
-P2_RANDOM = _p2_cases(12, 7003)
+def _p2_flash_cases(n, seed):
+    """bf16 D = 128 query partials on the flash kernel (g * Lq > 16): both
+    the 4-wave instance (g <= 4, g * Lq <= 128) and the 8-wave one."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        g = int(rng.choice([1, 2, 3, 4, 8]))
+        small = i % 2 == 0 and g <= 4          # alternate the two instances
+        if small:                              # 16 < g * Lq <= 128
+            Lq = int(rng.integers(16 // g + 1, 128 // g + 1))
+        else:                                  # 128 < g * Lq <= 200 + g
+            Lq = int(rng.integers(128 // g + 1, 200 // g + 2))
+        Hkv = int(rng.integers(1, 3))
+        B = int(rng.integers(1, 3))
+        L = int(rng.integers(1, 1500))
+        b = int(rng.integers(16, 600))
+        splits = int(rng.choice([1, 2, 3, 5, 8]))
+        out.append((B, g * Hkv, Hkv, 128, L, Lq, b, splits))
+    return out
+
+
+P2_RANDOM = _p2_cases(12, 7003) + _p2_flash_cases(10, 7005)
 
 
 @pytest.mark.parametrize("case", P2_RANDOM, ids=[str(i) for i in range(len(P2_RANDOM))])
