@@ -1131,7 +1131,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
                      "traffic": pmc_traffic(),
-                     "kernel": "flash2_kernel (Phase 1)"},
+                     "kernel": "flash2_kernel<8, 2> (Phase 1)"},
     }
     if w.rope and w.D == 128 and not args.phase1_only and not args.no_separate_rope:
         out["phase1"]["separate_rope"] = phase1_separate_rope(st, dev, w, ev)
