@@ -34,9 +34,9 @@
 //  * each step's softmax and next QK MFMAs run at a raised wave priority
 //    (s_setprio), the PV MFMAs at the normal one: the two waves of a SIMD
 //    then tend to alternate, one's VALU work beside the other's MFMAs
-//    (1.8-2.7% faster at 8B-128K than without, same box).  The V^T
-//    operands of the PV are read at the start of the step, before the
-//    softmax, so the PV MFMAs find them in registers (another ~0.4%).
+//    (1.8-2.7% faster at 8B-128K than without, same box).  Half of the
+//    V^T operands of the PV are read at the start of the step, before the
+//    softmax, so the first PV MFMAs find them in registers (another ~1%).
 //  * the softmax denominator is summed from the fp32 P before it is rounded
 //    to bf16 for the PV MFMA (summing the rounded P would move the lse by up
 //    to 2^-9 relative).
@@ -542,11 +542,14 @@ void flash2_kernel(const FlashParams p) {
     // of the two waves of a SIMD the one in its softmax goes ahead while the
     // other is in its PV MFMAs: the two fall into alternating phases.
     bf16x8 pf[2];
-    // the V^T operands of this sub-tile's PV are read first, so that the
-    // PV MFMAs below need no LDS wait (the sched barrier keeps the reads here)
+    // the V^T operands of the first half of this sub-tile's PV are read
+    // first, so that those PV MFMAs need no LDS wait and the reads of the
+    // second half complete under them (the sched barrier keeps the early
+    // reads here; hoisting all of them, or a quarter or three quarters,
+    // measured slower)
     bf16x8 va[D / 32][2];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 64; ++db)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const s16x4 a0 = tr_read(vofs[0][db] + CUR + cc * 16 * ROWB);
@@ -588,7 +591,15 @@ void flash2_kernel(const FlashParams p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) oacc[db] = mfma32(va[db][cc], pf[cc], oacc[db]);
+      for (int cc = 0; cc < 2; ++cc) {
+        if (db >= D / 64) {
+          const s16x4 a0 = tr_read(vofs[0][db] + CUR + cc * 16 * ROWB);
+          const s16x4 a1 = tr_read(vofs[1][db] + CUR + cc * 16 * ROWB);
+          va[db][cc] = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        oacc[db] = mfma32(va[db][cc], pf[cc], oacc[db]);
+      }
     if (__builtin_expect(more && mask_needed(j + 1), 0)) mask(j + 1, sn);
     s = sn;
   };
