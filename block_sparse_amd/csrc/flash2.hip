@@ -99,14 +99,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // M0 is a reserved register: the compiler neither saves it around the asm
 // nor needs it here (on gfx950 the LDS reads take no M0), so writing it is
 // safe as long as the kernel keeps no M0 value of its own; a host test
-// checks the generated code for exactly that.
+// checks the generated code for exactly that.  NT sets the nontemporal
+// hint, for K/V that no other workgroup reads again.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -343,7 +351,12 @@ void flash2_kernel(const FlashParams p) {
   };
   if (nt0 == 0) to_range_b();
   // the 4 DMAs of the next tile into buffer buf (every wave issues exactly 4
-  // loads per tile: wait_vm_keep4 relies on it)
+  // loads per tile: wait_vm_keep4 relies on it).  The 4-wave instance runs
+  // only Phase-2 query items, each of which streams its chunk's K/V once
+  // from HBM: its loads carry the nontemporal hint (at 8B-1M the query
+  // partials then read at 6.4-6.8 TB/s instead of 5.7).  Phase 1 re-reads
+  // the anchor's K/V from L2 and the Infinity Cache and keeps plain loads.
+  constexpr bool NT = SUB == 1;
   auto load_next = [&](int buf) {
     uint32_t dk[2], dv[2];
 #pragma unroll
@@ -355,15 +368,15 @@ void flash2_kernel(const FlashParams p) {
     if (__builtin_expect(lfull > 0, 1)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        dma16(lk, lok[i], dk[i]);
-        dma16(lv, lov[i], dv[i]);
+        dma16<NT>(lk, lok[i], dk[i]);
+        dma16<NT>(lv, lov[i], dv[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int64_t rr = min((int64_t)lrow[i], lrows - 1);
-        dma16(lk, (uint32_t)(rr * lks + lcolb[i]), dk[i]);
-        dma16(lv, (uint32_t)(rr * lvs + lcolb[i]), dv[i]);
+        dma16<NT>(lk, (uint32_t)(rr * lks + lcolb[i]), dk[i]);
+        dma16<NT>(lv, (uint32_t)(rr * lvs + lcolb[i]), dv[i]);
       }
     }
     lk += KT * lks;
