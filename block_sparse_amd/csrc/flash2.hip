@@ -19,8 +19,9 @@
 //    across each 16-lane group.
 //  * every LDS address is a per-lane register plus an immediate below
 //    64 KiB: the tile loop is unrolled over the three buffers, the K tiles
-//    and the V tiles sit in two 48 KiB arrays, and each array's address is
-//    folded into the per-lane registers, so no LDS read needs an add.
+//    and the V tiles sit in two arrays (48 KiB each with 64-key tiles), and
+//    each array's address is folded into the per-lane registers, so no LDS
+//    read needs an add.
 //  * which sub-tiles need the causal / range-end mask is decided from two
 //    32-bit thresholds computed once (64-bit compares would go to the VALU).
 //  * lazy online softmax tested after the fact: P_j is formed with the
@@ -207,6 +208,9 @@ __device__ __forceinline__ void rope_q_pass(bf16x8* qf, int j0, int FPP, int r, 
 // instance <8, 2> serves Phase 1 and the Phase-2 query; <4, 1> serves query
 // items whose rows fill at most 4 column blocks: with 48 KiB of LDS two of
 // its workgroups share a CU, so no wave computes columns without rows.
+// Both keep two waves per SIMD: amdgpu_waves_per_eu(2) holds the 4-wave
+// instance to the 256 registers that allows (without it the compiler takes
+// 284, and only one of its workgroups fits a CU).
 template <int NW, int SUB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void flash2_kernel(const FlashParams p) {
