@@ -516,6 +516,11 @@ def config_record(name, ev, rows_per_block=8, decode_steps=16):
         rec.update({"query_us": pq["us"], "query_frac_of_roofline": pq["frac_of_roofline"],
                     "query_splits": pq["splits"]})
     if n_dec:
+        # one untimed pass over the same steps first (each step rewrites its
+        # own cache row with the same values and sees only rows up to it, so
+        # the timed pass computes the same results), then the timed pass
+        for t in range(n_dec):
+            st.decode(t, qd[:, :, t:t + 1], kd[:, :, t:t + 1], vd[:, :, t:t + 1])
         e0, e1 = ev(), ev()
         e0.record()
         for t in range(n_dec):
